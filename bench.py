@@ -1,0 +1,278 @@
+"""Benchmark: KDA speculative verify + commit on one MI355X.
+
+A step is one pass of the whole path over one batch: kda_verify (window from
+the checkpoints, outputs and records) followed by kda_commit (accepted prefix
+replayed into the checkpoints). The default workload is the decode batch:
+B=64 requests, H=32 heads, K=V=128, T=4 tokens each (1 + 3 draft), bf16
+activations, fp32 checkpoints made by 64 random prefill tokens through the
+library's own recurrence, num_accepted ~ Binomial(4, 0.7).
+
+Inputs are resident in HBM before the timed region. To keep the 256 MB
+Infinity Cache (MALL) from serving the checkpoints, the steps rotate over
+several independent copies of the inputs (pools, activations, records), so
+consecutive steps touch different memory.
+
+Printed: one JSON line (metric, value = step tokens/s, per-kernel times,
+achieved HBM bandwidth against the 8 TB/s peak, and the CPU oracle's rate on a
+bounded sample of the same workload).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+STATE_BYTES = 128 * 128 * 4    # one (slot, head) fp32 state
+TOKEN_IN_BYTES = 4 * 128 * 2 + 2   # q, k, v, g (bf16 x 128) + beta, per token and head
+OUT_BYTES = 128 * 2                # o per token and head
+REC_BYTES = 3 * 128 * 2 + 2        # records k, v, g + beta per token and head
+
+
+def algorithmic_bytes(T, n_commit, valid, H):
+    """Bytes the method must move (each counted once).
+
+    verify: per valid (row, head) the state once, each token's inputs, its
+            output and its records: 65,536 + 2,052 * T_i.
+    commit: per valid (row, head) with n' > 0 the state read and written and
+            n' records read: 131,072 + 770 * n'.
+    """
+    T = np.asarray(T)[valid]
+    n = np.asarray(n_commit)[valid]
+    verify = H * np.sum(STATE_BYTES + (TOKEN_IN_BYTES + OUT_BYTES + REC_BYTES) * T)
+    commit = H * np.sum(np.where(n > 0, 2 * STATE_BYTES + REC_BYTES * n, 0))
+    return float(verify), float(commit)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=["decode", "deep", "ragged"])
+    ap.add_argument("--sets", type=int, default=6, help="independent input copies rotated")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU sample until this much wall time is spent")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path shards by requests and heads with "
+              "no exchange, and no multi-GPU run is part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_speculative_kda_amd as kda
+    from workloads import make_batch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    batch = make_batch(args.workload)
+    B, H, Q = batch.num_rows, batch.H, batch.Q
+    T = batch.seq_lens()
+    ntok = batch.tokens.num_tokens
+    valid = batch.valid_rows()
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    def up_bf16(bits):
+        return up(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+    layer = kda.Layer(a_log=up(batch.a_log), g_bias=up(batch.g_bias), scale=batch.scale,
+                      lower_bound=batch.lower_bound)
+    cu = up(batch.cu_seqlens)
+    si = up(batch.state_indices)
+    nacc = up(batch.num_accepted)
+    hk = H * 128
+
+    # ---- checkpoints: the prefill recipe runs the library's recurrence
+    pool0 = up(batch.initial_pool())
+    if batch.init == "prefill":
+        p = batch.prefill
+        qkv = up_bf16(p.qkv)
+        o_pre = torch.empty((p.num_tokens, H, 128), dtype=torch.bfloat16, device=dev)
+        kda.kda_recurrent(layer, qkv[:, :hk].view(-1, H, 128), qkv[:, hk:2 * hk].view(-1, H, 128),
+                          qkv[:, 2 * hk:].view(-1, H, 128), up_bf16(p.g), up_bf16(p.beta),
+                          up(batch.prefill_cu), pool0, si, o_pre)
+        torch.cuda.synchronize()
+        del qkv, o_pre
+
+    # ---- independent input sets (defeat the MALL between steps)
+    sets = []
+    for _ in range(args.sets):
+        qkv = up_bf16(batch.tokens.qkv)
+        sets.append(dict(
+            pool=pool0.clone(),
+            q=qkv[:, :hk].view(ntok, H, 128), k=qkv[:, hk:2 * hk].view(ntok, H, 128),
+            v=qkv[:, 2 * hk:].view(ntok, H, 128), g=up_bf16(batch.tokens.g),
+            beta=up_bf16(batch.tokens.beta), rec=kda.allocate_records(B, H, Q, dev),
+            o=torch.empty((ntok, H, 128), dtype=torch.bfloat16, device=dev), qkv=qkv))
+    del pool0
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def verify(s):
+        kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
+                       s["rec"], s["o"], stream=stream)
+
+    def commit(s):
+        kda.kda_commit(layer, cu, s["pool"], si, s["rec"], nacc, stream=stream)
+
+    for i in range(args.warmup):
+        s = sets[i % len(sets)]
+        verify(s)
+        commit(s)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, events around every launch on the launch stream
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        s = sets[i % len(sets)]
+        ev[i][0].record(stream)
+        verify(s)
+        ev[i][1].record(stream)
+        commit(s)
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    tv = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    tc = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+
+    n_commit = np.minimum(np.maximum(batch.num_accepted, 0), np.minimum(T, Q))
+    vbytes, cbytes = algorithmic_bytes(T, n_commit, valid, H)
+    tok_verify = int(T[valid].sum())
+    tok_commit = int(n_commit[valid].sum())
+    ms_step = total_ms / K
+    v_ms, c_ms = float(tv.mean()), float(tc.mean())
+    kernels = {
+        "kda_verify": dict(avg_us=v_ms * 1e3, median_us=float(np.median(tv)) * 1e3,
+                           bytes=vbytes, gbs=vbytes / (v_ms * 1e6),
+                           tokens_per_s=tok_verify / (v_ms * 1e-3)),
+        "kda_commit": dict(avg_us=c_ms * 1e3, median_us=float(np.median(tc)) * 1e3,
+                           bytes=cbytes, gbs=cbytes / (c_ms * 1e6),
+                           tokens_per_s=tok_commit / (c_ms * 1e-3)),
+    }
+    for kinfo in kernels.values():
+        kinfo["frac_of_peak"] = kinfo["gbs"] / PEAK_HBM_GBS
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+
+    # ---- achievable copy bandwidth on this GPU (context for the peak)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e6)
+    del src, dst
+
+    result = {
+        "metric": "KDA verify+commit tokens/s and achieved HBM GB/s vs peak (B=64,H=32,T=4)",
+        "value": tok_verify / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{batch.name}: B={B} H={H} K=V=128 T={'ragged' if batch.name == 'ragged' else int(T.max())} "
+                        f"Q={Q}, bf16 activations, fp32 checkpoints, one layer call per kernel",
+            "B": B, "H": H, "K": 128, "V": 128, "T": int(T.max()), "window": Q,
+            "verified_tokens_per_step": tok_verify, "committed_tokens_per_step": tok_commit,
+            "input_sets_rotated": len(sets),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": kernels[dom]["gbs"],
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": kernels[dom]["gbs"] / PEAK_HBM_GBS,
+            "traffic": None,
+        },
+        "kernels": kernels,
+        "step_gbs": (vbytes + cbytes) / (ms_step * 1e6),
+        "step_frac_of_peak": (vbytes + cbytes) / (ms_step * 1e6) / PEAK_HBM_GBS,
+        "commit_tokens_per_s": tok_commit / (c_ms * 1e-3),
+        "verify_tokens_per_s": tok_verify / (v_ms * 1e-3),
+        "copy_gbs_measured": copy_gbs,
+    }
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_rows, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(batch, rows, seconds):
+    """The oracle (NumPy fp64), as it stands, on the first `rows` rows of the
+    same workload: verify then commit, single-threaded, repeated until
+    `seconds` of wall time; scaled to tokens/s."""
+    from threadpoolctl import threadpool_limits
+    from oracle import kda_ref as ref
+
+    rows = min(rows, batch.num_rows)
+    lay = ref.Layer(batch.a_log, batch.g_bias, batch.scale, batch.lower_bound)
+    sel = np.zeros(batch.num_rows, bool)
+    sel[:rows] = True
+    si = np.where(sel, batch.state_indices, 0).astype(np.int32)
+    pool0 = batch.initial_pool()
+    if batch.init == "prefill":     # the sample's checkpoints, by the oracle (untimed)
+        p = batch.prefill
+        ref.kda_recurrent(lay, p.q, p.k, p.v, p.g, p.beta, batch.prefill_cu, pool0, si,
+                          np.zeros((p.num_tokens, batch.H, 128), np.uint16))
+    t = batch.tokens
+    T = batch.seq_lens()
+    toks = int(T[sel & (batch.state_indices > 0)].sum())
+    walls = []
+    with threadpool_limits(1):
+        while sum(walls) < seconds or len(walls) < 1:
+            pool = pool0.copy()
+            rec = ref.Records.empty(batch.num_rows, batch.H, batch.Q, 128)
+            o = np.zeros((t.num_tokens, batch.H, 128), np.uint16)
+            t0 = time.perf_counter()
+            ref.kda_verify(lay, t.q, t.k, t.v, t.g, t.beta, batch.cu_seqlens, pool, si, rec, o)
+            ref.kda_commit(lay, batch.cu_seqlens, t.num_tokens, pool, si, rec,
+                           batch.num_accepted)
+            walls.append(time.perf_counter() - t0)
+    wall = float(np.median(walls))
+    return {"value": toks / wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"verify+commit of {rows} of {batch.num_rows} rows ({toks} tokens, all "
+                      f"{batch.H} heads), NumPy fp64 on one thread, median of {len(walls)} runs "
+                      f"({wall:.2f} s each)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * kda.h -- C ABI of libkda: KDA (Kimi Delta Attention) speculative verify and
+ * accepted-token commit with one fp32 checkpoint state per request
+ * ("RecoverSSM"), hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * The method, per token and per head, with the state S of shape [K, V]
+ * (pages: "recoverssm.py (GLM-5.3-Flash KDA speculative verify with one
+ * checkpoint state per request)", _verify_kernel per-token loop):
+ *     q^ = scale * q / sqrt(sum(q*q) + 1e-6)      k^ = k / sqrt(sum(k*k) + 1e-6)
+ *     g  = lower_bound * sigmoid(exp(A_log) * (g_raw + g_bias))  (bounded gate)
+ *        | -exp(A_log) * softplus(g_raw + g_bias)                 (unbounded gate)
+ *     beta = sigmoid(beta_raw)
+ *     S = diag(exp(g)) S;  u = beta * (v - S^T k^);  S = S + k^ u^T;  o = S^T q^
+ * The unbounded gate is named but not printed on the kda.py page (layer
+ * constructor); the formula above is this library's reading of it.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer inside the structs and every array argument is a DEVICE
+ *   pointer unless marked "host". The structs themselves live in host memory
+ *   and are read only during the call.
+ * - bf16 values are passed as uint16_t bit patterns.
+ * - Token arrays: q, k, v, g are [num_tokens, H, 128] with the head stride
+ *   128 elements and a token stride given in elements (q/k/v may be column
+ *   blocks of one projection output); beta is [num_tokens, H] with a token
+ *   stride. o is dense [num_tokens, H, 128].
+ * - A request row i owns tokens [cu_seqlens[i], cu_seqlens[i+1]) (T_i of
+ *   them). A row with state_indices[i] <= 0 is skipped: nothing of it is read
+ *   or written (slot 0 is the null block). A row whose span is malformed
+ *   (negative start, end before start or beyond num_tokens) or whose slot is
+ *   >= num_slots is also skipped: the kernels range-check every index they
+ *   read from device memory, so bad metadata cannot make them access memory
+ *   out of bounds. Distinct rows must use distinct slots.
+ * - Checkpoint pool: fp32 [num_slots, H, V, K], K fastest (each (slot, head)
+ *   is one dense 128 x 128 block of 64 KiB; the stored block is S^T). The
+ *   slot stride is given in elements and must be a multiple of 4; the
+ *   pointer must be 16-byte aligned.
+ * - Records (raw bf16 inputs saved by verify for the commit; the record
+ *   layout is re-chosen head-major so that one (row, head) is contiguous):
+ *       k, g [rows+1, H, Q, 128], v [rows+1, H, Q, 128], beta [rows+1, H, Q]
+ *   where Q = window (tokens per record row). Record row r is stored at
+ *   index r + 1; index 0 is a scratch row: rows whose record row is -1 (or
+ *   out of range) write their records there and nothing reads it (pages:
+ *   "vllm.models.kimi_k3...recoverssm.context", allocate_records). Only the
+ *   first Q tokens of a row are recorded.
+ * - Calls are asynchronous on `stream`, enqueue at most one kernel, never
+ *   allocate, never synchronise and never abort. The caller owns every
+ *   buffer. The host checks below run before anything is enqueued; on any
+ *   error nothing is enqueued. num_rows == 0 returns KDA_OK with no launch.
+ * - Device metadata that the host cannot see (cu_seqlens, state_indices,
+ *   record_rows, num_accepted, pending, eager) is only range-checked inside
+ *   the kernels as described above.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,         /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,        /* inconsistent sizes (H <= 0, head_dim, window, strides, eager without pending) */
+  KDA_ERR_CAPACITY = 3,     /* more rows than record rows (identity record mapping) */
+  KDA_ERR_ALIGN = 4,        /* pointer or stride not aligned for the vector loads */
+  KDA_ERR_ALIAS = 5,        /* an output range overlaps an input or another output */
+  KDA_ERR_UNSUPPORTED = 6,  /* head_dim other than 128 */
+  KDA_ERR_LAUNCH = 7        /* the HIP launch reported an error */
+} kda_status;
+
+/* One layer's gate parameters (host struct). */
+typedef struct kda_layer {
+  int32_t num_heads;        /* H > 0 */
+  int32_t head_dim;         /* K == V; must be 128 */
+  float scale;              /* multiplies q^ (normally head_dim^-0.5) */
+  int32_t has_lower_bound;  /* 1: bounded gate with lower_bound; 0: unbounded gate */
+  float lower_bound;        /* e.g. -5; ignored when has_lower_bound == 0 */
+  const float* a_log;       /* [H] fp32 */
+  const float* g_bias;      /* [H * head_dim] fp32 */
+} kda_layer;
+
+/* A packed ragged batch of raw activations (host struct of device pointers). */
+typedef struct kda_tokens {
+  const uint16_t* q;        /* [num_tokens, H, K] bf16, token stride stride_q */
+  const uint16_t* k;        /* [num_tokens, H, K] bf16, token stride stride_k */
+  const uint16_t* v;        /* [num_tokens, H, V] bf16, token stride stride_v */
+  const uint16_t* g;        /* [num_tokens, H, K] bf16 raw gate, token stride stride_g */
+  const uint16_t* beta;     /* [num_tokens, H] bf16 raw beta, token stride stride_beta */
+  int64_t stride_q, stride_k, stride_v, stride_g, stride_beta;   /* elements */
+  const int32_t* cu_seqlens;  /* [num_rows + 1] int32 */
+  int32_t num_rows;
+  int32_t num_tokens;       /* rows of the token arrays (and of o) */
+} kda_tokens;
+
+/* The checkpoint pool of one layer (host struct of device pointers). */
+typedef struct kda_pool {
+  float* state;                  /* [num_slots, H, 128, 128] fp32, K fastest */
+  int64_t slot_stride;           /* elements between slots, >= H*128*128, multiple of 4 */
+  int32_t num_slots;
+  const int32_t* state_indices;  /* [num_rows] int32 slot per row; <= 0: skip the row */
+} kda_pool;
+
+/* Raw bf16 records (host struct of device pointers); pointers are the
+ * allocation bases, i.e. the scratch row at index 0. */
+typedef struct kda_records {
+  uint16_t* k;              /* [rows + 1, H, window, 128] */
+  uint16_t* v;              /* [rows + 1, H, window, 128] */
+  uint16_t* g;              /* [rows + 1, H, window, 128] */
+  uint16_t* beta;           /* [rows + 1, H, window] */
+  int32_t rows;             /* record rows (not counting the scratch row) */
+  int32_t window;           /* Q: tokens per record row, 1..64 */
+} kda_records;
+
+/*
+ * kda_recurrent -- the plain full-state recurrence (pages: recoverssm.py,
+ * _verify_kernel's per-token body, which is the stock fused recurrent KDA
+ * kernel's; kda.py, the plain-decode call of the recurrent kernel).
+ * For each valid row: load the row's checkpoint, run all T_i tokens (any
+ * length), write o for each token, store the final state into the slot in
+ * place. It is the equivalence reference of kda_commit: committing n tokens
+ * gives the same bits as kda_recurrent over those n tokens.
+ *   o: [num_tokens, H, 128] bf16 output; rows that are skipped are not written.
+ * Errors: NULL -> KDA_ERR_NULL; head_dim != 128 -> KDA_ERR_UNSUPPORTED;
+ * H <= 0, negative sizes or strides too small -> KDA_ERR_SHAPE; misaligned
+ * (state 16 B, q/k/v/g 8 B with token strides multiple of 4) -> KDA_ERR_ALIGN;
+ * o overlapping the pool or a token array -> KDA_ERR_ALIAS.
+ */
+kda_status kda_recurrent(const kda_layer* layer, const kda_tokens* tokens,
+                         const kda_pool* pool, uint16_t* o, hipStream_t stream);
+
+/*
+ * kda_verify -- speculative verify from the checkpoint (pages: recoverssm.py,
+ * module docstring and _verify_kernel / kda_recoverssm_verify). For each valid
+ * row: run its T_i window tokens from the checkpoint, write o, and write the
+ * raw k, v, g, beta of tokens 0..min(T_i, Q)-1 to record row r, where
+ * r = record_rows[i] (record_rows == NULL: r = i, which needs
+ * num_rows <= rec->rows, else KDA_ERR_CAPACITY). The pool is read only: no
+ * state is written.
+ * Errors as kda_recurrent, plus: records overlapping o, the pool or the
+ * token arrays -> KDA_ERR_ALIAS; misaligned records -> KDA_ERR_ALIGN.
+ */
+kda_status kda_verify(const kda_layer* layer, const kda_tokens* tokens,
+                      const kda_pool* pool, const kda_records* rec,
+                      const int32_t* record_rows, uint16_t* o, hipStream_t stream);
+
+/*
+ * kda_commit -- commit the accepted prefix (pages: recoverssm.py,
+ * _prepare_commit_plan_kernel and Glm5NextRecoverSSMCommitContext.commit;
+ * deferred mode: recoverssm.context, KDADeferredCommitContext.commit).
+ * For row i: T_i from cu_seqlens, n' = min(max(num_accepted[i], 0), T_i, Q),
+ * r = record_rows ? record_rows[i] : i. The row is valid when its slot is in
+ * (0, num_slots), n' > 0 and 0 <= r < rec->rows.
+ *  - pending == NULL: every valid row replays records 0..n'-1 of record row r
+ *    from its slot and stores the state into the slot in place.
+ *  - pending != NULL (deferred): for 0 <= r < rec->rows,
+ *    pending[r] = eager[i] ? 0 : (valid ? n' : 0); rows with eager[i] != 0
+ *    are committed now as above; the others wait for kda_verify_deferred.
+ *    eager == NULL: no row is eager.
+ *   num_accepted: [num_rows] int32; pending: [rec->rows] int32, indexed by
+ *   record row; eager: [num_rows] uint8 mask.
+ * Errors: NULL pointers -> KDA_ERR_NULL; eager without pending ->
+ * KDA_ERR_SHAPE; record_rows == NULL with num_rows > rec->rows ->
+ * KDA_ERR_CAPACITY; the pool overlapping the records -> KDA_ERR_ALIAS.
+ */
+kda_status kda_commit(const kda_layer* layer, const int32_t* cu_seqlens, int32_t num_rows,
+                      const kda_pool* pool, const kda_records* rec,
+                      const int32_t* record_rows, const int32_t* num_accepted,
+                      int32_t* pending, const uint8_t* eager, hipStream_t stream);
+
+/*
+ * kda_verify_deferred -- fold the pending commit, then verify, in one pass
+ * (pages: recoverssm.context, module summary and KDARecoverSSMDeferred: the
+ * next verify replays the pending commit in the same pass).
+ * For each row with a slot in (0, num_slots): r = record_rows[i];
+ * p = min(max(pending[r], 0), rec_prev->window) when 0 <= r < rec_prev->rows,
+ * else 0. Replay records 0..p-1 of rec_prev row r from the slot; if p > 0
+ * store the state into the slot. Then verify the row's T_i tokens from that
+ * state exactly as kda_verify does, writing o and rec_next row r. With
+ * every T_i == 0 this is the flush (fold only). pending is read only.
+ * rec_prev and rec_next must be different buffers with the same rows, window.
+ * Errors as kda_verify, plus: rec_prev overlapping rec_next -> KDA_ERR_ALIAS;
+ * mismatched rows/window -> KDA_ERR_SHAPE.
+ */
+kda_status kda_verify_deferred(const kda_layer* layer, const kda_tokens* tokens,
+                               const kda_pool* pool, const kda_records* rec_prev,
+                               const int32_t* pending, const kda_records* rec_next,
+                               const int32_t* record_rows, uint16_t* o, hipStream_t stream);
+
+/* Host: a static, human-readable name for a status code. */
+const char* kda_status_string(kda_status status);
+
+/* Host: the library's build identification (static string). */
+const char* kda_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

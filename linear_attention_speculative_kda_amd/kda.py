@@ -1,0 +1,241 @@
+"""Python front end of libkda: the four calls of include/kda.h, taking torch
+tensors that live on the GPU. Marshalling only; the computation is in HIP.
+
+Tensor conventions (K = V = 128):
+  q, k, v, g      [num_tokens, H, K] bf16 (or any 2-byte dtype holding bf16
+                  bits), head stride K, element stride 1, any token stride that
+                  is a multiple of 4 (q/k/v may be column blocks of one
+                  projection output); g must be the same shape.
+  beta            [num_tokens, H], element stride 1.
+  o               [num_tokens, H, V] bf16, dense.
+  cu_seqlens      int32 [num_rows + 1]; state_indices int32 [num_rows].
+  pool            fp32 [num_slots, H, V, K], inner dims dense.
+  Records         raw bf16 records with a scratch row at index 0.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+HEAD_DIM = 128
+
+
+@dataclass
+class Layer:
+    a_log: torch.Tensor          # fp32 [H]
+    g_bias: torch.Tensor         # fp32 [H * K]
+    scale: float
+    lower_bound: float | None = None   # None: unbounded softplus gate
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.a_log.numel())
+
+    def c_struct(self) -> _lib.KdaLayer:
+        _need(self.a_log, torch.float32, "a_log")
+        _need(self.g_bias, torch.float32, "g_bias")
+        if self.g_bias.numel() != self.num_heads * HEAD_DIM:
+            raise ValueError("g_bias must hold H * 128 values")
+        return _lib.KdaLayer(
+            num_heads=self.num_heads, head_dim=HEAD_DIM, scale=float(self.scale),
+            has_lower_bound=0 if self.lower_bound is None else 1,
+            lower_bound=0.0 if self.lower_bound is None else float(self.lower_bound),
+            a_log=self.a_log.data_ptr(), g_bias=self.g_bias.data_ptr())
+
+
+@dataclass
+class Records:
+    """Raw records: k, g, v [rows+1, H, window, K] and beta [rows+1, H, window]
+    (bf16); index 0 is the scratch row of record row -1."""
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.k.shape[0] - 1
+
+    @property
+    def window(self) -> int:
+        return self.k.shape[2]
+
+    def c_struct(self) -> _lib.KdaRecords:
+        for name in ("k", "v", "g", "beta"):
+            t = getattr(self, name)
+            if t.element_size() != 2 or not t.is_contiguous():
+                raise ValueError(f"records.{name} must be a contiguous 2-byte tensor")
+        return _lib.KdaRecords(k=self.k.data_ptr(), v=self.v.data_ptr(), g=self.g.data_ptr(),
+                               beta=self.beta.data_ptr(), rows=self.rows, window=self.window)
+
+
+def allocate_records(rows: int, num_heads: int, window: int, device,
+                     dtype: torch.dtype = torch.bfloat16) -> Records:
+    shape = (rows + 1, num_heads, window, HEAD_DIM)
+    return Records(k=torch.empty(shape, dtype=dtype, device=device),
+                   v=torch.empty(shape, dtype=dtype, device=device),
+                   g=torch.empty(shape, dtype=dtype, device=device),
+                   beta=torch.empty(shape[:3], dtype=dtype, device=device))
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _act(t: torch.Tensor, name: str, H: int) -> int:
+    """Check a [tokens, H, K] activation view; return its token stride."""
+    if t.element_size() != 2:
+        raise TypeError(f"{name} must hold bf16 (2-byte) values")
+    if t.dim() != 3 or t.shape[1] != H or t.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be [tokens, {H}, {HEAD_DIM}], got {tuple(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
+        raise ValueError(f"{name} needs head stride {HEAD_DIM} and element stride 1")
+    return t.stride(0)
+
+
+def _tokens(q, k, v, g, beta, cu_seqlens, H: int) -> _lib.KdaTokens:
+    n = q.shape[0]
+    for t, name in ((k, "k"), (v, "v"), (g, "g")):
+        if t.shape[0] != n:
+            raise ValueError(f"{name} has {t.shape[0]} tokens, q has {n}")
+    if beta.element_size() != 2 or beta.dim() != 2 or beta.shape != (n, H) or (n > 0 and beta.stride(1) != 1):
+        raise ValueError("beta must be [tokens, H] of bf16 with element stride 1")
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    return _lib.KdaTokens(
+        q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), g=g.data_ptr(), beta=beta.data_ptr(),
+        stride_q=_act(q, "q", H), stride_k=_act(k, "k", H), stride_v=_act(v, "v", H),
+        stride_g=_act(g, "g", H), stride_beta=beta.stride(0) if n > 0 else H,
+        cu_seqlens=cu_seqlens.data_ptr(), num_rows=cu_seqlens.numel() - 1, num_tokens=n)
+
+
+def _pool(pool: torch.Tensor, state_indices: torch.Tensor, H: int, rows: int | None = None) -> _lib.KdaPool:
+    if pool.dtype != torch.float32 or pool.dim() != 4 or pool.shape[1:] != (H, HEAD_DIM, HEAD_DIM):
+        raise ValueError(f"pool must be fp32 [slots, {H}, {HEAD_DIM}, {HEAD_DIM}]")
+    if pool.stride()[1:] != (HEAD_DIM * HEAD_DIM, HEAD_DIM, 1):
+        raise ValueError("pool inner dims must be dense")
+    _need(state_indices, torch.int32, "state_indices")
+    if rows is not None and state_indices.numel() < rows:
+        raise ValueError(f"state_indices has {state_indices.numel()} entries, needs {rows}")
+    return _lib.KdaPool(state=pool.data_ptr(), slot_stride=pool.stride(0),
+                        num_slots=pool.shape[0], state_indices=state_indices.data_ptr())
+
+
+def _opt_ptr(t: torch.Tensor | None, dtype, name: str, min_len: int = 0):
+    if t is None:
+        return None
+    _need(t, dtype, name)
+    if t.numel() < min_len:
+        raise ValueError(f"{name} has {t.numel()} entries, needs {min_len}")
+    return t.data_ptr()
+
+
+def _on_gpu(ref: torch.Tensor, *tensors) -> None:
+    """Every tensor handed to the kernels must live on the pool's GPU: a host
+    pointer would be dereferenced by the device."""
+    if not ref.is_cuda:
+        raise ValueError("tensors must be on a GPU")
+    for t in tensors:
+        if t is None:
+            continue
+        if isinstance(t, Records):
+            _on_gpu(ref, t.k, t.v, t.g, t.beta)
+        elif isinstance(t, Layer):
+            _on_gpu(ref, t.a_log, t.g_bias)
+        elif t.device != ref.device:
+            raise ValueError(f"tensor on {t.device}, expected {ref.device}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _out(o: torch.Tensor, n: int, H: int) -> int:
+    if o.element_size() != 2 or not o.is_contiguous() or o.shape != (n, H, HEAD_DIM):
+        raise ValueError(f"o must be a contiguous bf16 [{n}, {H}, {HEAD_DIM}] tensor")
+    return o.data_ptr()
+
+
+def kda_recurrent(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indices, o,
+                  stream=None) -> None:
+    """Plain recurrence: o for every token, final state stored in place."""
+    _on_gpu(pool, layer, q, k, v, g, beta, cu_seqlens, state_indices, o)
+    lib = _lib.load()
+    H = layer.num_heads
+    L, T, P = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H), _pool(pool, state_indices, H, cu_seqlens.numel() - 1)
+    st = lib.kda_recurrent(ctypes.byref(L), ctypes.byref(T), ctypes.byref(P),
+                           _out(o, q.shape[0], H), _stream(stream))
+    _lib.check("kda_recurrent", st)
+
+
+def kda_verify(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indices,
+               rec: Records, o, record_rows=None, stream=None) -> None:
+    """Verify from the checkpoints: o and raw records; the pool is read only."""
+    _on_gpu(pool, layer, q, k, v, g, beta, cu_seqlens, state_indices, rec, o, record_rows)
+    lib = _lib.load()
+    H = layer.num_heads
+    L, T, P = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H), _pool(pool, state_indices, H, cu_seqlens.numel() - 1)
+    R = rec.c_struct()
+    st = lib.kda_verify(ctypes.byref(L), ctypes.byref(T), ctypes.byref(P), ctypes.byref(R),
+                        _opt_ptr(record_rows, torch.int32, "record_rows", cu_seqlens.numel() - 1),
+                        _out(o, q.shape[0], H), _stream(stream))
+    _lib.check("kda_verify", st)
+
+
+def kda_commit(layer: Layer, cu_seqlens, pool, state_indices, rec: Records, num_accepted,
+               record_rows=None, pending=None, eager=None, stream=None) -> None:
+    """Commit the accepted prefix (or, with ``pending``, defer it)."""
+    _on_gpu(pool, layer, cu_seqlens, state_indices, rec, num_accepted, record_rows, pending, eager)
+    lib = _lib.load()
+    H = layer.num_heads
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    L, P, R = layer.c_struct(), _pool(pool, state_indices, H, cu_seqlens.numel() - 1), rec.c_struct()
+    st = lib.kda_commit(ctypes.byref(L), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                        ctypes.byref(P), ctypes.byref(R),
+                        _opt_ptr(record_rows, torch.int32, "record_rows", cu_seqlens.numel() - 1),
+                        _opt_ptr(num_accepted, torch.int32, "num_accepted", cu_seqlens.numel() - 1),
+                        _opt_ptr(pending, torch.int32, "pending", rec.rows),
+                        _opt_ptr(eager, torch.uint8, "eager", cu_seqlens.numel() - 1), _stream(stream))
+    _lib.check("kda_commit", st)
+
+
+def kda_verify_deferred(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indices,
+                        rec_prev: Records, pending, rec_next: Records, o, record_rows=None,
+                        stream=None) -> None:
+    """Fold the pending replays into the checkpoints, then verify."""
+    _on_gpu(pool, layer, q, k, v, g, beta, cu_seqlens, state_indices, rec_prev, pending,
+            rec_next, o, record_rows)
+    lib = _lib.load()
+    H = layer.num_heads
+    L, T, P = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H), _pool(pool, state_indices, H, cu_seqlens.numel() - 1)
+    Rp, Rn = rec_prev.c_struct(), rec_next.c_struct()
+    st = lib.kda_verify_deferred(ctypes.byref(L), ctypes.byref(T), ctypes.byref(P),
+                                 ctypes.byref(Rp), _opt_ptr(pending, torch.int32, "pending", rec_prev.rows),
+                                 ctypes.byref(Rn), _opt_ptr(record_rows, torch.int32, "record_rows", cu_seqlens.numel() - 1),
+                                 _out(o, q.shape[0], H), _stream(stream))
+    _lib.check("kda_verify_deferred", st)
+
+
+def kda_flush(layer: Layer, pool, state_indices, rec_prev: Records, pending, rec_next: Records,
+              record_rows=None, stream=None) -> None:
+    """Fold every pending replay without verifying anything: kda_verify_deferred
+    with an empty window on every row."""
+    dev = pool.device
+    n = state_indices.numel()
+    H = layer.num_heads
+    empty = torch.empty((0, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(n + 1, dtype=torch.int32, device=dev)
+    kda_verify_deferred(layer, empty, empty, empty, empty,
+                        torch.empty((0, H), dtype=torch.bfloat16, device=dev), cu, pool,
+                        state_indices, rec_prev, pending, rec_next, empty, record_rows, stream)

@@ -1,0 +1,185 @@
+"""CPU checks of the C ABI: the library loads, exports every call that
+include/kda.h declares, and rejects bad arguments on the host before anything
+is enqueued (no GPU needed: the pointers below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_speculative_kda_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libkda.so not built")
+
+E = {name: code for code, name in _lib.STATUS_NAMES.items()}
+A = 0x10000000  # fake, aligned device addresses (never dereferenced on the host)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    fns = declared_functions()
+    for name in ("kda_recurrent", "kda_verify", "kda_commit", "kda_verify_deferred",
+                 "kda_status_string"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    lib = _lib.load()
+    for f in declared_functions():
+        assert hasattr(lib, f)
+
+
+def test_status_strings():
+    for code, name in _lib.STATUS_NAMES.items():
+        assert _lib.status_string(code).startswith(name)
+    assert "unknown" in _lib.status_string(99)
+
+
+# ------------------------------------------------------------ validation --
+
+H, K = 4, 128
+
+
+def layer(**kw):
+    d = dict(num_heads=H, head_dim=K, scale=K ** -0.5, has_lower_bound=0, lower_bound=0.0,
+             a_log=A, g_bias=A + 0x1000)
+    d.update(kw)
+    return _lib.KdaLayer(**d)
+
+
+def tokens(n_tok=8, n_rows=2, **kw):
+    hk = H * K
+    d = dict(q=A + 0x100000, k=A + 0x100000 + 2 * hk, v=A + 0x100000 + 4 * hk,
+             g=A + 0x200000, beta=A + 0x300000, stride_q=3 * hk, stride_k=3 * hk,
+             stride_v=3 * hk, stride_g=hk, stride_beta=H, cu_seqlens=A + 0x400000,
+             num_rows=n_rows, num_tokens=n_tok)
+    d.update(kw)
+    return _lib.KdaTokens(**d)
+
+
+def pool(**kw):
+    d = dict(state=A + 0x1000000, slot_stride=H * K * K, num_slots=5, state_indices=A + 0x500000)
+    d.update(kw)
+    return _lib.KdaPool(**d)
+
+
+def records(base=A + 0x8000000, rows=4, window=4, **kw):
+    per = (rows + 1) * H * window * K * 2
+    d = dict(k=base, v=base + per, g=base + 2 * per, beta=base + 3 * per, rows=rows, window=window)
+    d.update(kw)
+    return _lib.KdaRecords(**d)
+
+
+O = A + 0x4000000   # an output range away from everything else
+
+
+def verify(L=None, T=None, P=None, R=None, rr=None, o=O):
+    lib = _lib.load()
+    return lib.kda_verify(ctypes.byref(L or layer()), ctypes.byref(T or tokens()),
+                          ctypes.byref(P or pool()), ctypes.byref(R or records()), rr, o, None)
+
+
+def test_verify_rejects_bad_layer():
+    lib = _lib.load()
+    assert lib.kda_verify(None, ctypes.byref(tokens()), ctypes.byref(pool()),
+                          ctypes.byref(records()), None, O, None) == E["KDA_ERR_NULL"]
+    assert verify(L=layer(head_dim=64)) == E["KDA_ERR_UNSUPPORTED"]
+    assert verify(L=layer(num_heads=0)) == E["KDA_ERR_SHAPE"]
+    assert verify(L=layer(a_log=0)) == E["KDA_ERR_NULL"]
+
+
+def test_verify_rejects_bad_tokens():
+    assert verify(T=tokens(q=0)) == E["KDA_ERR_NULL"]
+    assert verify(T=tokens(stride_q=100)) == E["KDA_ERR_SHAPE"]           # < H*K
+    assert verify(T=tokens(stride_g=H * K + 2)) == E["KDA_ERR_ALIGN"]     # not a multiple of 4
+    assert verify(T=tokens(k=A + 0x100000 + 2 * H * K + 2)) == E["KDA_ERR_ALIGN"]
+    assert verify(T=tokens(num_rows=-1)) == E["KDA_ERR_SHAPE"]
+
+
+def test_verify_rejects_bad_pool_and_records():
+    assert verify(P=pool(state=A + 0x1000004)) == E["KDA_ERR_ALIGN"]
+    assert verify(P=pool(slot_stride=H * K * K - 4)) == E["KDA_ERR_SHAPE"]
+    assert verify(P=pool(slot_stride=H * K * K + 2)) == E["KDA_ERR_ALIGN"]
+    assert verify(R=records(window=0)) == E["KDA_ERR_SHAPE"]
+    assert verify(R=records(window=65)) == E["KDA_ERR_SHAPE"]
+    assert verify(R=records(k=0)) == E["KDA_ERR_NULL"]
+    # identity record rows need num_rows <= rows
+    assert verify(T=tokens(n_rows=5), R=records(rows=4)) == E["KDA_ERR_CAPACITY"]
+
+
+def test_verify_rejects_aliasing():
+    # o overlapping the token arrays, the pool or the records
+    assert verify(o=A + 0x100000 + 64) == E["KDA_ERR_ALIAS"]
+    assert verify(o=A + 0x1000000 + 1024) == E["KDA_ERR_ALIAS"]
+    assert verify(o=A + 0x8000000 + 2) == E["KDA_ERR_ALIAS"]
+    # records overlapping each other
+    r = records()
+    r.v = r.k + 64
+    assert verify(R=r) == E["KDA_ERR_ALIAS"]
+
+
+def test_empty_batch_is_a_no_op():
+    # num_rows == 0 returns OK before anything is enqueued (no GPU touched)
+    assert verify(T=tokens(n_rows=0, num_tokens=0)) == E["KDA_OK"]
+    lib = _lib.load()
+    assert lib.kda_recurrent(ctypes.byref(layer()), ctypes.byref(tokens(n_rows=0)),
+                             ctypes.byref(pool()), O, None) == E["KDA_OK"]
+    assert lib.kda_commit(ctypes.byref(layer()), A, 0, ctypes.byref(pool()),
+                          ctypes.byref(records()), None, A, None, None, None) == E["KDA_OK"]
+    # per-row arrays may be NULL when there are no rows
+    assert verify(T=tokens(n_rows=0, num_tokens=0), P=pool(state_indices=0)) == E["KDA_OK"]
+    assert lib.kda_commit(ctypes.byref(layer()), A, 0, ctypes.byref(pool(state_indices=0)),
+                          ctypes.byref(records()), None, None, None, None, None) == E["KDA_OK"]
+
+
+def test_commit_validation():
+    lib = _lib.load()
+    c = lambda **kw: lib.kda_commit(  # noqa: E731
+        ctypes.byref(kw.get("L", layer())), kw.get("cu", A), kw.get("n", 2),
+        ctypes.byref(kw.get("P", pool())), ctypes.byref(kw.get("R", records())),
+        kw.get("rr"), kw.get("acc", A + 0x600000), kw.get("pending"), kw.get("eager"), None)
+    assert c(cu=0) == E["KDA_ERR_NULL"]
+    assert c(acc=0) == E["KDA_ERR_NULL"]
+    assert c(n=-1) == E["KDA_ERR_SHAPE"]
+    assert c(eager=A + 0x700000) == E["KDA_ERR_SHAPE"]               # eager without pending
+    assert c(n=5, R=records(rows=4)) == E["KDA_ERR_CAPACITY"]
+    assert c(R=records(base=A + 0x1000000)) == E["KDA_ERR_ALIAS"]    # records inside the pool
+    assert c(pending=A + 0x1000000) == E["KDA_ERR_ALIAS"]            # pending inside the pool
+
+
+def test_verify_deferred_validation():
+    lib = _lib.load()
+
+    def d(rp=None, rn=None, pending=A + 0x700000, o=O):
+        return lib.kda_verify_deferred(ctypes.byref(layer()), ctypes.byref(tokens()),
+                                       ctypes.byref(pool()), ctypes.byref(rp or records()),
+                                       pending, ctypes.byref(rn or records(base=A + 0xC000000)),
+                                       None, o, None)
+    assert d(pending=0) == E["KDA_ERR_NULL"]
+    assert d(rn=records()) == E["KDA_ERR_ALIAS"]                       # rec_prev == rec_next
+    assert d(rn=records(base=A + 0xC000000, window=8)) == E["KDA_ERR_SHAPE"]
+    assert d(rn=records(base=A + 0xC000000, rows=3)) == E["KDA_ERR_SHAPE"]
+    assert d(pending=A + 0xC000000) == E["KDA_ERR_ALIAS"]              # pending inside rec_next
+    assert d(o=A + 0xC000000) == E["KDA_ERR_ALIAS"]
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

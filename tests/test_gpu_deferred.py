@@ -1,0 +1,138 @@
+"""GPU parity of the deferred commit: several layers, several steps, a pending
+replay folded into the next verify, eager rows committed at once, and a
+final flush; against the oracle's sequential (eager) replay and, bitwise,
+against the GPU's own eager flow."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_speculative_kda_amd as kda
+from oracle import kda_ref as ref
+from workloads import make_deferred
+
+from .helpers import (DevTokens, bits_host, check_o, check_state, dev_records, oracle_records,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_layer(run, layer):
+    p = run.params[layer]
+    return kda.Layer(a_log=to_dev(p.a_log), g_bias=to_dev(p.g_bias), scale=run.scale,
+                     lower_bound=run.lower_bound)
+
+
+def gpu_flows(run):
+    """Run the deferred and the eager flow on the GPU; return per (layer, step)
+    outputs and the final pools of both."""
+    B, H, Q = run.B, run.H, run.Q
+    si = to_dev(run.state_indices)
+    rr = to_dev(run.record_rows)
+    cu = to_dev(run.cu_seqlens)
+    layers = [dev_layer(run, l) for l in range(run.layers)]
+    pools_d, pools_e = [], []
+    for l in range(run.layers):
+        p = to_dev(run.initial_pool(l))
+        pools_d.append(p)
+        pools_e.append(p.clone())
+    recs_d = [[dev_records(B, H, Q), dev_records(B, H, Q)] for _ in range(run.layers)]
+    recs_e = [dev_records(B, H, Q) for _ in range(run.layers)]
+    pending = torch.zeros(B, dtype=torch.int32, device=DEV)
+    outs_d, outs_e = {}, {}
+    ntok = B * run.T
+    for s in range(run.steps):
+        nacc = to_dev(run.num_accepted(s))
+        eager = to_dev(run.eager(s))
+        toks = [DevTokens(run.tokens(l, s)) for l in range(run.layers)]
+        for l in range(run.layers):
+            od = torch.empty((ntok, H, 128), dtype=torch.bfloat16, device=DEV)
+            kda.kda_verify_deferred(layers[l], *toks[l].args(), cu, pools_d[l], si,
+                                    recs_d[l][(s + 1) % 2], pending, recs_d[l][s % 2], od,
+                                    record_rows=rr)
+            oe = torch.empty_like(od)
+            kda.kda_verify(layers[l], *toks[l].args(), cu, pools_e[l], si, recs_e[l], oe,
+                           record_rows=rr)
+            outs_d[l, s], outs_e[l, s] = od, oe
+        for l in range(run.layers):
+            kda.kda_commit(layers[l], cu, pools_d[l], si, recs_d[l][s % 2], nacc, record_rows=rr,
+                           pending=pending, eager=eager)
+            kda.kda_commit(layers[l], cu, pools_e[l], si, recs_e[l], nacc, record_rows=rr)
+        torch.cuda.synchronize()
+        # pending[r] = 0 for eager rows, n' otherwise
+        n = np.minimum(np.maximum(run.num_accepted(s), 0), run.Q)
+        want = np.zeros(B, np.int32)
+        want[run.record_rows] = np.where(run.eager(s) != 0, 0, n)
+        assert np.array_equal(pending.cpu().numpy(), want), f"pending after step {s}"
+    last = (run.steps - 1) % 2
+    for l in range(run.layers):
+        kda.kda_flush(layers[l], pools_d[l], si, recs_d[l][last], pending, recs_d[l][1 - last],
+                      record_rows=rr)
+    torch.cuda.synchronize()
+    return outs_d, outs_e, pools_d, pools_e
+
+
+def oracle_flow(run, layer, rows):
+    """Sequential replay of one layer for the given rows (others skipped)."""
+    B, H, Q = run.B, run.H, run.Q
+    p = run.params[layer]
+    lay = ref.Layer(p.a_log, p.g_bias, run.scale, run.lower_bound)
+    si = np.zeros(B, np.int32)
+    si[rows] = run.state_indices[rows]
+    pool = np.zeros((run.num_slots, H, 128, 128), np.float32)
+    for r in rows:
+        pool[si[r]] = run.slot_state(layer, int(si[r]))
+    outs = []
+    for s in range(run.steps):
+        t = run.tokens(layer, s)
+        o = np.zeros((B * run.T, H, 128), np.uint16)
+        rec = oracle_records(B, H, Q)
+        ref.kda_verify(lay, t.q, t.k, t.v, t.g, t.beta, run.cu_seqlens, pool, si, rec, o,
+                       record_rows=run.record_rows)
+        ref.kda_commit(lay, run.cu_seqlens, B * run.T, pool, si, rec, run.num_accepted(s),
+                       record_rows=run.record_rows)
+        outs.append(o)
+    return outs, pool
+
+
+def compare(run, outs_d, outs_e, pools_d, pools_e, sample):
+    for key in outs_d:
+        assert torch.equal(outs_d[key].view(torch.int16), outs_e[key].view(torch.int16)), \
+            f"deferred o differs from eager o at (layer, step) {key}"
+    for l in range(run.layers):
+        assert torch.equal(pools_d[l].view(torch.int32), pools_e[l].view(torch.int32)), \
+            f"deferred pool differs from eager pool, layer {l}"
+    for layer, rows in sample:
+        say(f"  oracle replay layer {layer} rows {rows}")
+        outs, pool = oracle_flow(run, layer, rows)
+        for s in range(run.steps):
+            og = bits_host(outs_d[layer, s])
+            for r in rows:
+                sl = slice(r * run.T, (r + 1) * run.T)
+                check_o(og[sl], outs[s][sl], what=f"o layer {layer} step {s} row {r}")
+        pg = pools_d[layer].cpu().numpy()
+        for r in rows:
+            slot = int(run.state_indices[r])
+            check_state(pg[slot], pool[slot], what=f"state layer {layer} row {r}")
+
+
+def test_deferred_small_all_rows():
+    run = make_deferred(B=24, H=4, layers=2, steps=4)
+    say("case deferred B=24 H=4 layers=2 steps=4")
+    res = gpu_flows(run)
+    compare(run, *res, sample=[(0, list(range(24))), (1, list(range(24)))])
+
+
+def test_deferred_full_size():
+    run = make_deferred()
+    say(f"case deferred B={run.B} H={run.H} layers={run.layers} steps={run.steps}")
+    res = gpu_flows(run)
+    compare(run, *res, sample=[(0, [0, 17, 300]), (5, [42, 511]), (7, [9])])
