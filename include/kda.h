@@ -80,7 +80,7 @@ typedef struct kda_layer {
   int32_t has_lower_bound;  /* 1: bounded gate with lower_bound; 0: unbounded gate */
   float lower_bound;        /* e.g. -5; ignored when has_lower_bound == 0 */
   const float* a_log;       /* [H] fp32 */
-  const float* g_bias;      /* [H * head_dim] fp32 */
+  const float* g_bias;      /* [H * head_dim] fp32, 16-byte aligned */
 } kda_layer;
 
 /* A packed ragged batch of raw activations (host struct of device pointers). */

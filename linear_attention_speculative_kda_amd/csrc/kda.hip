@@ -37,6 +37,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "kda.h"
 
 namespace {
@@ -96,6 +98,9 @@ struct Params {
 
 // ---------------------------------------------------------------- helpers --
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
@@ -105,32 +110,53 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return (uint16_t)(u >> 16);
 }
 
+// Hardware transcendentals (v_exp_f32 = 2^x, v_log_f32 = log2 x, v_rcp_f32,
+// v_rsq_f32; about 1 ulp each). Every call of the library goes through the
+// same functions, so all of them round alike.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// log(1 + y) for y >= 0 with a relative error of a few ulp even for tiny y:
+// log(u) * y / (u - 1) with u = 1 + y rounded (the correction cancels the
+// rounding of u).
+__device__ __forceinline__ float log1p_hw(float y) {
+  const float u = 1.0f + y;
+  const float l = __builtin_amdgcn_logf(u) * kLn2;
+  return u == 1.0f ? y : l * (y * rcp_hw(u - 1.0f));
+}
+
+__device__ __forceinline__ float sigmoid_hw(float x) { return rcp_hw(1.0f + exp_hw(-x)); }
+
+// Decay factor exp(g) of one key channel from x = g_raw + g_bias, A = exp(A_log).
+//   bounded:   g = lb * sigmoid(A x)
+//   unbounded: g = -A * softplus(x), softplus(x) = max(x, 0) + log1p(exp(-|x|))
+__device__ __forceinline__ float decay_of(float x, float A, int has_lb, float lb) {
+  if (has_lb) return exp_hw(lb * sigmoid_hw(A * x));
+  const float sp = fmaxf(x, 0.0f) + log1p_hw(exp_hw(-fabsf(x)));
+  return exp_hw(-(A * sp));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 8 lanes of a group; every lane gets the same bits.
+// Sum over the 8 lanes of a group; every lane gets the same bits (each step
+// adds the same two operands in both partner lanes).
 __device__ __forceinline__ float reduce8(float x) {
   x = x + dpp<0xB1>(x);   // quad_perm [1,0,3,2]
   x = x + dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x = x + dpp<0x141>(x);  // row_half_mirror
+  x = x + dpp<0x141>(x);  // row_half_mirror: lane i <-> 7-i
   return x;
-}
-
-template <int XOR>
-__device__ __forceinline__ float swz(float x) {
-  // ds_swizzle bit mode: lane j of each 32-lane half reads lane j ^ XOR.
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (XOR << 10) | 0x1F));
 }
 
 // Sum over the 32 lanes of a half-wave; every lane gets the same bits.
 __device__ __forceinline__ float reduce32(float x) {
-  x = x + swz<1>(x);
-  x = x + swz<2>(x);
-  x = x + swz<4>(x);
-  x = x + swz<8>(x);
-  x = x + swz<16>(x);
+  x = reduce8(x);
+  x = x + dpp<0x140>(x);  // row_mirror: lane i <-> 15-i (the other 8-group)
+  // ds_swizzle bit mode, xor 16: lane j reads lane j ^ 16 (the other row)
+  x = x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (16 << 10) | 0x1F));
   return x;
 }
 
@@ -141,57 +167,395 @@ __device__ __forceinline__ void unpack4(uint2 raw, float out[4]) {
   out[3] = bf16_to_f32(raw.y >> 16);
 }
 
-__device__ __forceinline__ float sum_sq4(const float x[4]) {
-  float s = x[0] * x[0];
-  s = fmaf(x[1], x[1], s);
-  s = fmaf(x[2], x[2], s);
-  s = fmaf(x[3], x[3], s);
+__device__ __forceinline__ float dot4(const float a[4], const float b[4]) {
+  float s = a[0] * b[0];
+  s = fmaf(a[1], b[1], s);
+  s = fmaf(a[2], b[2], s);
+  s = fmaf(a[3], b[3], s);
   return s;
 }
 
-// Gate of one key channel from x = g_raw + g_bias (A = exp(A_log)).
-__device__ __forceinline__ float gate_of(float x, float A, int has_lb, float lb) {
-  if (has_lb) {
-    // bounded: lb * sigmoid(A * x), written lb / (1 + exp(-(A * x)))
-    return lb / (1.0f + expf(-(A * x)));
+// LDS staging area for one chunk of up to NT tokens.
+template <int BV, int NT>
+struct Stage {
+  float kh[NT][KD];   // k^
+  float qh[NT][KD];   // q^ (scale folded in)
+  float dk[NT][KD];   // exp(g)
+  float vt[NT][BV];   // the tile's slice of v
+  float bt[NT];       // beta
+};
+
+// The chunk-form verify additionally keeps, for the window's tokens t and
+// s <= t (Gamma_t = the decay product over tokens 1..t, P(s,t) the product
+// over tokens s+1..t, both diagonal over key channels):
+//   al[t] = Gamma_t k^_t,  ga[t] = Gamma_t q^_t,
+//   M[t][s] = k^_s . P(s,t) k^_t  (s < t),   N[t][s] = k^_s . P(s,t) q^_t.
+//   w[s] = P(s,m) k^_s and gm = Gamma_m for the state after the chunk.
+template <int BV, int NT>
+struct StageChunk : Stage<BV, NT> {
+  float al[NT][KD];
+  float ga[NT][KD];
+  float w[NT][KD];
+  float gm[KD];
+  float M[NT][NT];
+  float N[NT][NT];
+};
+
+// Per-workgroup constants.
+struct Ctx {
+  int bos, ri, head, tile, H;
+  float A;            // exp(A_log[head])
+  int tid, wave, p8, grp, hw, l32;
+};
+
+// Sum over K of x[k] * y[k] for one value row: 16 channels in this lane,
+// then the 8 lanes of the row group.
+__device__ __forceinline__ float row_dot(const float x[16], const float y[16]) {
+  float acc[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float a = x[4 * jj] * y[4 * jj];
+    a = fmaf(x[4 * jj + 1], y[4 * jj + 1], a);
+    a = fmaf(x[4 * jj + 2], y[4 * jj + 2], a);
+    a = fmaf(x[4 * jj + 3], y[4 * jj + 3], a);
+    acc[jj] = a;
   }
-  // unbounded: -A * softplus(x), softplus(x) = max(x, 0) + log1p(exp(-|x|))
-  const float sp = fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
-  return -(A * sp);
+  return reduce8((acc[0] + acc[1]) + (acc[2] + acc[3]));
 }
 
-// LDS staging area for one chunk of tokens.
+// Read this lane's 16 key channels of an LDS vector.
+__device__ __forceinline__ void lds_row16(const float* vec, int p8, float out[16]) {
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float4 a = *reinterpret_cast<const float4*>(vec + jj * 32 + p8 * 4);
+    out[4 * jj + 0] = a.x; out[4 * jj + 1] = a.y; out[4 * jj + 2] = a.z; out[4 * jj + 3] = a.w;
+  }
+}
+
+__device__ __forceinline__ int row_in_tile(int rr, const Ctx& c) {
+  return (rr * NWAVES + c.wave) * 8 + c.grp;
+}
+
+template <int R, int BV>
+__device__ __forceinline__ void load_tile(float (&S)[R][16], const float* sbase, const Ctx& c) {
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const float* src = sbase + (c.tile * BV + row_in_tile(rr, c)) * KD + c.p8 * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 x = *reinterpret_cast<const float4*>(src + j * 32);
+      S[rr][4 * j + 0] = x.x; S[rr][4 * j + 1] = x.y; S[rr][4 * j + 2] = x.z; S[rr][4 * j + 3] = x.w;
+    }
+  }
+}
+
+template <int R, int BV>
+__device__ __forceinline__ void store_tile(const float (&S)[R][16], float* sbase, const Ctx& c) {
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    float* dst = sbase + (c.tile * BV + row_in_tile(rr, c)) * KD + c.p8 * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4 x;
+      x.x = S[rr][4 * j + 0]; x.y = S[rr][4 * j + 1]; x.z = S[rr][4 * j + 2]; x.w = S[rr][4 * j + 3];
+      *reinterpret_cast<float4*>(dst + j * 32) = x;
+    }
+  }
+}
+
+// One staged token's raw inputs in registers (a half-wave per token, 4
+// channels per lane).
 template <int BV>
-struct Stage {
-  float kh[CH][KD];   // k^
-  float qh[CH][KD];   // q^ (scale folded in)
-  float dk[CH][KD];   // exp(g)
-  float vt[CH][BV];   // the tile's slice of v
-  float bt[CH];       // beta
+struct Raw {
+  uint2 k, g, q;
+  float4 gb;          // g_bias of the lane's 4 key channels
+  uint16_t v[BV / 32];
+  uint16_t b;
+  bool active;
 };
 
-// Where one token's raw inputs come from.
-struct Src {
-  const uint16_t* k;
-  const uint16_t* g;
-  const uint16_t* v;
-  const uint16_t* b;
-  const uint16_t* q;  // nullptr: no output for this token
-};
+// Issue the loads of tokens c0 .. c0+m-1 of a segment. fold: records of
+// storage row ri (no q); otherwise window tokens bos + j.
+template <int MODE, int BV>
+__device__ __forceinline__ void stage_load(Raw<BV>& x, const Params& p, const Ctx& c, bool fold,
+                                           int c0, int m) {
+  constexpr int VPL = BV / 32;
+  x.active = c.hw < m;
+  if (!x.active) return;
+  const int j = c0 + c.hw, l32 = c.l32;
+  const uint16_t *k, *g, *v, *b, *q = nullptr;
+  if (fold) {
+    const long long base = ((long long)c.ri * c.H + c.head) * p.Q + j;
+    k = ((MODE == kDeferred) ? p.pk : p.rk) + base * KD;
+    g = ((MODE == kDeferred) ? p.pg : p.rg) + base * KD;
+    v = ((MODE == kDeferred) ? p.pv : p.rv) + base * KD;
+    b = ((MODE == kDeferred) ? p.pb : p.rb) + base;
+  } else {
+    const long long tok = (long long)c.bos + j;
+    k = p.k + tok * p.sk + c.head * KD;
+    g = p.g + tok * p.sg + c.head * KD;
+    v = p.v + tok * p.sv + c.head * KD;
+    b = p.beta + tok * p.sb + c.head;
+    q = p.q + tok * p.sq + c.head * KD;
+  }
+  x.k = *reinterpret_cast<const uint2*>(k + 4 * l32);
+  x.g = *reinterpret_cast<const uint2*>(g + 4 * l32);
+  x.gb = *reinterpret_cast<const float4*>(p.g_bias + c.head * KD + 4 * l32);
+  x.q = fold ? make_uint2(0, 0) : *reinterpret_cast<const uint2*>(q + 4 * l32);
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) x.v[e] = v[c.tile * BV + l32 * VPL + e];
+  x.b = (l32 == 0) ? *b : (uint16_t)0;
+}
+
+// Turn the loaded raw inputs into the per-token vectors in LDS; for window
+// tokens of the verify modes also write the raw inputs to the records (first
+// Q tokens only).
+template <int MODE, int BV, int NT>
+__device__ __forceinline__ void stage_compute(Stage<BV, NT>& st, const Raw<BV>& x, const Params& p,
+                                              const Ctx& c, bool fold, int c0) {
+  constexpr int VPL = BV / 32;
+  if (!x.active) return;
+  const int hw = c.hw, l32 = c.l32, j = c0 + hw;
+  float kx[4], gx[4];
+  unpack4(x.k, kx);
+  unpack4(x.g, gx);
+  const float kinv = rsqrt_hw(reduce32(dot4(kx, kx)) + 1e-6f);
+  float4 kh, dk;
+  kh.x = kx[0] * kinv; kh.y = kx[1] * kinv; kh.z = kx[2] * kinv; kh.w = kx[3] * kinv;
+  dk.x = decay_of(gx[0] + x.gb.x, c.A, p.has_lb, p.lower_bound);
+  dk.y = decay_of(gx[1] + x.gb.y, c.A, p.has_lb, p.lower_bound);
+  dk.z = decay_of(gx[2] + x.gb.z, c.A, p.has_lb, p.lower_bound);
+  dk.w = decay_of(gx[3] + x.gb.w, c.A, p.has_lb, p.lower_bound);
+  *reinterpret_cast<float4*>(&st.kh[hw][4 * l32]) = kh;
+  *reinterpret_cast<float4*>(&st.dk[hw][4 * l32]) = dk;
+  if (!fold) {
+    float qx[4];
+    unpack4(x.q, qx);
+    const float qinv = rsqrt_hw(reduce32(dot4(qx, qx)) + 1e-6f);
+    float4 qh;
+    qh.x = (qx[0] * qinv) * p.scale; qh.y = (qx[1] * qinv) * p.scale;
+    qh.z = (qx[2] * qinv) * p.scale; qh.w = (qx[3] * qinv) * p.scale;
+    *reinterpret_cast<float4*>(&st.qh[hw][4 * l32]) = qh;
+  }
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) st.vt[hw][l32 * VPL + e] = bf16_to_f32(x.v[e]);
+  if (l32 == 0) st.bt[hw] = sigmoid_hw(bf16_to_f32(x.b));
+  if ((MODE == kVerify || MODE == kDeferred) && !fold && j < p.Q) {
+    const long long base = ((long long)c.ri * c.H + c.head) * p.Q + j;
+    if (c.tile == 0) {
+      *reinterpret_cast<uint2*>(p.rk + base * KD + 4 * l32) = x.k;
+      *reinterpret_cast<uint2*>(p.rg + base * KD + 4 * l32) = x.g;
+      if (l32 == 0) p.rb[base] = x.b;
+    }
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) p.rv[base * KD + c.tile * BV + l32 * VPL + e] = x.v[e];
+  }
+}
+
+// The per-token recurrence over m staged tokens, state in registers. With
+// `out`, token t's output goes to o[tok0 + t].
+template <int R, int BV, int NT>
+__device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT>& st, const Params& p,
+                                           const Ctx& c, int m, bool out, long long tok0) {
+  for (int t = 0; t < m; ++t) {
+    float kh[16], dk[16];
+    lds_row16(st.kh[t], c.p8, kh);
+    lds_row16(st.dk[t], c.p8, dk);
+    const float beta = st.bt[t];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      // decay the key channels
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[rr][e] = S[rr][e] * dk[e];
+      // delta rule against the decayed state, then the rank-1 update
+      const float kv = row_dot(S[rr], kh);
+      const float u = beta * (st.vt[t][row_in_tile(rr, c)] - kv);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[rr][e] = fmaf(kh[e], u, S[rr][e]);
+    }
+    if (out) {
+      float qh[16];
+      lds_row16(st.qh[t], c.p8, qh);
+      uint16_t* orow = p.o + ((tok0 + t) * c.H + c.head) * KD + c.tile * BV;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const float ov = row_dot(S[rr], qh);
+        if (c.p8 == 0) orow[row_in_tile(rr, c)] = f32_to_bf16(ov);
+      }
+    }
+  }
+}
+
+// Verify of a chunk of m <= TMAX staged tokens from the state in registers.
+// Unrolling the recurrence from the chunk's start state S0:
+//   a_t = (Gamma_t S0)^T k^_t,  b_t = (Gamma_t S0)^T q^_t
+//   u_t = beta_t (v_t - a_t - sum_{s<t} M[t][s] u_s)
+//   o_t = b_t + sum_{s<=t} N[t][s] u_s
+// which is the per-token loop's math (decay, delta rule, update, output)
+// with 2m dot products per value row instead of 4m passes over it. With
+// `more`, the state is advanced to the chunk's end for the next chunk:
+//   S_m = Gamma_m S0 + sum_s P(s,m) k^_s u_s^T.
+// Outputs go to o[tok0 + t].
+template <int R, int BV, int TMAX, int NT>
+__device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, NT>& st,
+                                             const Params& p, const Ctx& c, int T,
+                                             long long tok0, bool more) {
+  // Decayed vectors: threads 0..127, one key channel each (all of the
+  // channel's staged values are read first, then a short product chain).
+  if (c.tid < KD) {
+    const int ch = c.tid;
+    float kk[TMAX], qq[TMAX], dd[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        kk[t] = st.kh[t][ch];
+        qq[t] = st.qh[t][ch];
+        dd[t] = st.dk[t][ch];
+      }
+    }
+    float gam = 1.0f;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        gam = gam * dd[t];
+        st.al[t][ch] = gam * kk[t];
+        st.ga[t][ch] = gam * qq[t];
+      }
+    }
+    if (more) {
+      st.gm[ch] = gam;
+      float pr = 1.0f;
+#pragma unroll
+      for (int t = TMAX - 1; t >= 0; --t) {
+        if (t < T) {
+          st.w[t][ch] = pr * kk[t];
+          pr = pr * dd[t];
+        }
+      }
+    }
+  }
+  // Coefficients: the T(T+1)/2 pairs (s, t), s <= t, numbered t(t+1)/2 + s,
+  // are dealt to the 8 half-waves; each lane covers 4 key channels. The pair
+  // is chosen by the half-wave's data (LDS addresses), not by branching, so
+  // both halves of a wave run the same instructions.
+  {
+    const int l = c.l32;
+    float4 dk4[TMAX];
+#pragma unroll
+    for (int r = 0; r < TMAX; ++r)
+      dk4[r] = (r < T) ? *reinterpret_cast<const float4*>(&st.dk[r][4 * l]) : make_float4(1.f, 1.f, 1.f, 1.f);
+    const int npairs = T * (T + 1) / 2;
+    constexpr int kSlots = (TMAX * (TMAX + 1) / 2 + 7) / 8;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      const int q = c.hw + 8 * j;
+      const bool live = q < npairs;
+      // pair number q -> (s, t): t is the largest with t(t+1)/2 <= q
+      int t = 0;
+#pragma unroll
+      for (int u = 1; u < TMAX; ++u) t += (u * (u + 1) / 2 <= q) ? 1 : 0;
+      const int sidx = live ? q - t * (t + 1) / 2 : 0;
+      const int tidx = live ? t : 0;
+      float4 w = *reinterpret_cast<const float4*>(&st.kh[sidx][4 * l]);
+#pragma unroll
+      for (int r = 1; r < TMAX; ++r) {
+        if (r > sidx && r <= tidx) {
+          w.x *= dk4[r].x; w.y *= dk4[r].y; w.z *= dk4[r].z; w.w *= dk4[r].w;
+        }
+      }
+      const float4 x = *reinterpret_cast<const float4*>(&st.qh[tidx][4 * l]);
+      const float4 y = *reinterpret_cast<const float4*>(&st.kh[tidx][4 * l]);
+      float nts = w.x * x.x;
+      nts = fmaf(w.y, x.y, nts);
+      nts = fmaf(w.z, x.z, nts);
+      nts = fmaf(w.w, x.w, nts);
+      float mts = w.x * y.x;
+      mts = fmaf(w.y, y.y, mts);
+      mts = fmaf(w.z, y.z, mts);
+      mts = fmaf(w.w, y.w, mts);
+      nts = reduce32(nts);
+      mts = reduce32(mts);
+      if (live && l == 0) {
+        st.N[tidx][sidx] = nts;
+        st.M[tidx][sidx] = sidx < tidx ? mts : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2T dot products per value row against the chunk's start state.
+  float a[R][TMAX], b[R][TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    if (t < T) {
+      float v16[16];
+      lds_row16(st.al[t], c.p8, v16);
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) a[rr][t] = row_dot(S[rr], v16);
+      lds_row16(st.ga[t], c.p8, v16);
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) b[rr][t] = row_dot(S[rr], v16);
+    }
+  }
+  // The T x T triangular recurrence per value row; lane p8 of the group
+  // stores token p8's output.
+  float u[R][TMAX];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int vloc = row_in_tile(rr, c);
+    float mine = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        float x = st.vt[t][vloc] - a[rr][t];
+#pragma unroll
+        for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[rr][s], x);
+        u[rr][t] = st.bt[t] * x;
+        float y = b[rr][t];
+#pragma unroll
+        for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[rr][s], y);
+        if (c.p8 == t) mine = y;
+      }
+    }
+    if (c.p8 < T)
+      p.o[((tok0 + c.p8) * c.H + c.head) * KD + c.tile * BV + vloc] = f32_to_bf16(mine);
+  }
+  if (more) {
+    float g16[16];
+    lds_row16(st.gm, c.p8, g16);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[rr][e] = S[rr][e] * g16[e];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        lds_row16(st.w[t], c.p8, g16);
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) S[rr][e] = fmaf(g16[e], u[rr][t], S[rr][e]);
+      }
+    }
+  }
+}
 
 // ------------------------------------------------------------------ kernel --
 
-template <int MODE, int R>
+template <int MODE, int R, int TMAX>
 __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
   constexpr int BV = R * NWAVES * 8;   // value rows per workgroup
-  constexpr int VPL = BV / 32;         // v values per lane when staging
-  __shared__ Stage<BV> st;
+  constexpr bool kChunk = (MODE == kVerify || MODE == kDeferred);
+  using StageT = typename std::conditional<kChunk, StageChunk<BV, CH>, Stage<BV, CH>>::type;
+  __shared__ StageT st;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int p8 = lane & 7;    // position inside the 8-lane row group
-  const int grp = lane >> 3;  // row group inside the wave
+  Ctx c;
+  c.tid = threadIdx.x;
+  c.wave = c.tid >> 6;
+  c.p8 = c.tid & 7;           // position inside the 8-lane row group
+  c.grp = (c.tid & 63) >> 3;  // row group inside the wave
+  c.hw = c.tid >> 5;          // half-wave: token slot when staging
+  c.l32 = c.tid & 31;         // 4 channels per lane when staging
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
   // consecutive logical blocks (the V-tiles and heads of one request) are
@@ -199,21 +563,22 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
   int b = blockIdx.x;
   const int nb = p.total_blocks;
   if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
-  const int tile = b % p.tiles;
+  c.tile = b % p.tiles;
   const int rh = b / p.tiles;
-  const int head = rh % p.H;
+  c.head = rh % p.H;
   const int row = rh / p.H;
-  const int H = p.H;
+  c.H = p.H;
 
   // ---- row prologue: span, slot, record row, counts -----------------------
   const int bos = p.cu[row];
   const int eos = p.cu[row + 1];
   int T = eos - bos;
   if (bos < 0 || T < 0 || (MODE != kCommit && eos > p.num_tokens)) T = 0;
+  c.bos = bos;
   const int slot = p.slots[row];
   const bool slot_ok = slot > 0 && slot < p.num_slots;
   const int r = p.record_rows ? p.record_rows[row] : row;
-  const int ri = (r >= 0 && r < p.rec_rows) ? r + 1 : 0;   // storage index, 0 = scratch
+  c.ri = (r >= 0 && r < p.rec_rows) ? r + 1 : 0;   // storage index, 0 = scratch
 
   int nfold = 0;   // records replayed into the state (commit / deferred fold)
   int nmain = 0;   // window tokens run with outputs (recurrent / verify)
@@ -222,16 +587,17 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
     n = n < 0 ? 0 : n;
     n = n < T ? n : T;
     n = n < p.Q ? n : p.Q;
-    const bool valid = slot_ok && n > 0 && ri > 0;
+    const bool valid = slot_ok && n > 0 && c.ri > 0;
     bool now = true;
     if (p.pending) {
       now = p.eager != nullptr && p.eager[row] != 0;
-      if (ri > 0 && head == 0 && tile == 0 && tid == 0) p.pending[ri - 1] = now ? 0 : (valid ? n : 0);
+      if (c.ri > 0 && c.head == 0 && c.tile == 0 && c.tid == 0)
+        p.pending[c.ri - 1] = now ? 0 : (valid ? n : 0);
     }
     nfold = (valid && now) ? n : 0;
   } else if (MODE == kDeferred) {
-    if (ri > 0) {
-      int pn = p.pending_in[ri - 1];
+    if (c.ri > 0) {
+      int pn = p.pending_in[c.ri - 1];
       pn = pn < 0 ? 0 : pn;
       nfold = pn < p.Q ? pn : p.Q;
     }
@@ -240,183 +606,217 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
     nmain = T;
   }
   if (!slot_ok || (nfold == 0 && nmain == 0)) return;
+  c.A = exp_hw(p.a_log[c.head]);
+  float* sbase = p.state + (long long)slot * p.slot_stride + (long long)c.head * KD * KD;
+  const bool chunk = kChunk && nmain <= TMAX;
 
-  // ---- state tile: issue the loads ----------------------------------------
-  float* sbase = p.state + (long long)slot * p.slot_stride + (long long)head * KD * KD;
+  // The first chunk's token loads go out before the state tile's: loads
+  // complete in issue order, so the staging math then waits for its own
+  // inputs only while the 64 KiB tile is still in flight.
+  Raw<BV> raw;
+  const bool first_fold = nfold > 0;
+  stage_load<MODE, BV>(raw, p, c, first_fold, 0, first_fold ? (nfold < CH ? nfold : CH)
+                                                             : (nmain < CH ? nmain : CH));
+  __builtin_amdgcn_sched_barrier(0);
   float S[R][16];
+  load_tile<R, BV>(S, sbase, c);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- fold: replay records into the state (commit, deferred fold) --------
+  if (nfold > 0) {
+    for (int c0 = 0; c0 < nfold; c0 += CH) {
+      const int m = (nfold - c0) < CH ? (nfold - c0) : CH;
+      if (c0 > 0) stage_load<MODE, BV>(raw, p, c, true, c0, m);
+      __syncthreads();  // the previous chunk is consumed
+      stage_compute<MODE, BV, CH>(st, raw, p, c, true, c0);
+      __syncthreads();
+      seq_tokens<R, BV, CH>(S, st, p, c, m, false, 0);
+    }
+    store_tile<R, BV>(S, sbase, c);
+    if (nmain > 0) stage_load<MODE, BV>(raw, p, c, false, 0, nmain < CH ? nmain : CH);
+  }
+
+  // ---- window: outputs (recurrent, verify, deferred verify) ---------------
+  if (nmain > 0) {
+    if constexpr (kChunk) {
+      if (chunk) {
+        __syncthreads();
+        stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0);
+        __syncthreads();
+        chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos, false);
+        return;
+      }
+    }
+    for (int c0 = 0; c0 < nmain; c0 += CH) {
+      const int m = (nmain - c0) < CH ? (nmain - c0) : CH;
+      if (c0 > 0) stage_load<MODE, BV>(raw, p, c, false, c0, m);
+      __syncthreads();
+      stage_compute<MODE, BV, CH>(st, raw, p, c, false, c0);
+      __syncthreads();
+      seq_tokens<R, BV, CH>(S, st, p, c, m, true, (long long)bos + c0);
+    }
+    if (MODE == kRecurrent) store_tile<R, BV>(S, sbase, c);
+  }
+}
+
+// ------------------------------------------------------- persistent verify --
+//
+// kda_verify reads each 64 KiB state once and writes no state, so the state
+// loads must overlap the per-head math for the kernel to run at the speed of
+// HBM. A fixed grid (as many workgroups as fit on the chip) walks the
+// (row, head, tile) items with a stride. Each item's state tile is streamed
+// straight into an LDS landing buffer (global_load_lds_dwordx4: each lane's
+// 16 bytes land at base + 16 * lane, one KiB per wave instruction) while the
+// previous item is computed; at the start of an item the tile moves from LDS
+// into registers and the buffer is refilled with the next item's tile.
+
+struct Item {
+  int row, head, tile, bos, T, ri;
+  float A;                  // exp(A_log[head])
+  const float* tile_base;   // first value row of the item's state tile
+  bool valid;
+};
+
+// An item's metadata is fetched with one vector load per lane (lane 0:
+// cu_seqlens[row], 1: cu_seqlens[row+1], 2: the slot, 3: the record row,
+// 4: A_log[head]) two items ahead, so that it never waits on scalar loads,
+// which share a counter with LDS.
+__device__ __forceinline__ int meta_issue(const Params& p, int it, int lane) {
+  if (it >= p.total_blocks) return 0;
+  const int rh = it / p.tiles;
+  const int head = rh % p.H;
+  const int row = rh / p.H;
+  const int* src = p.cu + row;
+  if (lane == 1) src = p.cu + row + 1;
+  if (lane == 2) src = p.slots + row;
+  if (lane == 3 && p.record_rows) src = p.record_rows + row;
+  if (lane == 4) src = reinterpret_cast<const int*>(p.a_log) + head;
+  const int v = *src;
+  return (lane == 3 && !p.record_rows) ? row : v;
+}
+
+__device__ __forceinline__ Item item_decode(const Params& p, int it, int mv, int BV) {
+  Item m;
+  m.valid = false;
+  m.T = 0;
+  m.A = 1.0f;
+  m.tile_base = nullptr;
+  if (it >= p.total_blocks) return m;
+  m.tile = it % p.tiles;
+  const int rh = it / p.tiles;
+  m.head = rh % p.H;
+  m.row = rh / p.H;
+  const int bos = __builtin_amdgcn_readlane(mv, 0);
+  const int eos = __builtin_amdgcn_readlane(mv, 1);
+  const int slot = __builtin_amdgcn_readlane(mv, 2);
+  const int r = __builtin_amdgcn_readlane(mv, 3);
+  m.A = exp_hw(__int_as_float(__builtin_amdgcn_readlane(mv, 4)));
+  int T = eos - bos;
+  if (bos < 0 || T < 0 || eos > p.num_tokens) T = 0;
+  m.bos = bos;
+  m.T = T;
+  m.ri = (r >= 0 && r < p.rec_rows) ? r + 1 : 0;
+  m.valid = slot > 0 && slot < p.num_slots && T > 0;
+  if (m.valid)
+    m.tile_base = p.state + (long long)slot * p.slot_stride + (long long)m.head * KD * KD +
+                  (long long)m.tile * BV * KD;
+  return m;
+}
+
+__device__ __forceinline__ void item_ctx(Ctx& c, const Item& m) {
+  c.bos = m.bos;
+  c.ri = m.ri;
+  c.head = m.head;
+  c.tile = m.tile;
+}
+
+// Issue an item's loads: the first chunk of token inputs into registers, the
+// state tile into the LDS landing buffer (rows 2g and 2g+1 per instruction).
+template <int BV, int TMAX>
+__device__ __forceinline__ void item_issue(const Item& m, Raw<BV>& raw, float* land,
+                                           const Params& p, Ctx c) {
+  if (!m.valid) return;
+  item_ctx(c, m);
+  stage_load<kVerify, BV>(raw, p, c, false, 0, m.T < TMAX ? m.T : TMAX);
+  constexpr int NI = BV / (2 * NWAVES);   // landing instructions per wave
+  const int lane = c.tid & 63;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int g = c.wave * NI + i;
+    const float* src = m.tile_base + 2 * g * KD + lane * 4;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(land + 2 * g * KD),
+                                     16, 0, 0);
+  }
+}
+
+template <int R, int BV>
+__device__ __forceinline__ void land_to_regs(float (&S)[R][16], const float* land, const Ctx& c) {
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
-    const int vrow = tile * BV + (rr * NWAVES + wave) * 8 + grp;
-    const float* src = sbase + vrow * KD + p8 * 4;
+    const float* src = land + row_in_tile(rr, c) * KD + c.p8 * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float4 x = *reinterpret_cast<const float4*>(src + j * 32);
-      S[rr][4 * j + 0] = x.x;
-      S[rr][4 * j + 1] = x.y;
-      S[rr][4 * j + 2] = x.z;
-      S[rr][4 * j + 3] = x.w;
+      S[rr][4 * j + 0] = x.x; S[rr][4 * j + 1] = x.y; S[rr][4 * j + 2] = x.z; S[rr][4 * j + 3] = x.w;
     }
   }
+}
 
-  const float A = expf(p.a_log[head]);
-  const int hw = tid >> 5;      // half-wave: token slot when staging
-  const int l32 = tid & 31;     // 4 channels per lane when staging
-  const float* gb = p.g_bias + head * KD + 4 * l32;
+template <int R, int TMAX>
+__global__ __launch_bounds__(NTHREADS) void verify_persistent(Params p) {
+  constexpr int BV = R * NWAVES * 8;
+  __shared__ StageChunk<BV, TMAX> st;
+  __shared__ __attribute__((aligned(16))) float land[BV * KD];
+  Ctx c;
+  c.tid = threadIdx.x;
+  c.wave = c.tid >> 6;
+  c.p8 = c.tid & 7;
+  c.grp = (c.tid & 63) >> 3;
+  c.hw = c.tid >> 5;
+  c.l32 = c.tid & 31;
+  c.H = p.H;
 
-  // Two segments: the fold (records, no output) then the main window.
-  for (int seg = 0; seg < 2; ++seg) {
-    const bool fold = seg == 0;
-    const int n = fold ? nfold : nmain;
-    if (n == 0) continue;
-    for (int c0 = 0; c0 < n; c0 += CH) {
-      const int m = (n - c0) < CH ? (n - c0) : CH;
-      __syncthreads();  // the previous chunk is consumed
-      // ---- stage: one token per half-wave --------------------------------
-      if (hw < m) {
-        const int j = c0 + hw;
-        Src s;
-        if (fold) {
-          const uint16_t* rk = (MODE == kDeferred) ? p.pk : p.rk;
-          const uint16_t* rg = (MODE == kDeferred) ? p.pg : p.rg;
-          const uint16_t* rv = (MODE == kDeferred) ? p.pv : p.rv;
-          const uint16_t* rb = (MODE == kDeferred) ? p.pb : p.rb;
-          const long long base = ((long long)ri * H + head) * p.Q + j;
-          s.k = rk + base * KD;
-          s.g = rg + base * KD;
-          s.v = rv + base * KD;
-          s.b = rb + base;
-          s.q = nullptr;
-        } else {
-          const long long tok = (long long)bos + j;
-          s.k = p.k + tok * p.sk + head * KD;
-          s.g = p.g + tok * p.sg + head * KD;
-          s.v = p.v + tok * p.sv + head * KD;
-          s.b = p.beta + tok * p.sb + head;
-          s.q = p.q + tok * p.sq + head * KD;
+  const int G = gridDim.x;
+  const int lane = c.tid & 63;
+  int it = blockIdx.x;
+  Raw<BV> raw;
+  Item cur = item_decode(p, it, meta_issue(p, it, lane), BV);
+  int mv_next = meta_issue(p, it + G, lane);
+  item_issue<BV, TMAX>(cur, raw, land, p, c);
+  float S[R][16];
+  while (it < p.total_blocks) {
+    // The item's tile and inputs have landed (this also drains the previous
+    // item's stores, long done by now).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (cur.valid) land_to_regs<R, BV>(S, land, c);
+    __syncthreads();   // the landing buffer and the staging area are free
+    const Item nxt = item_decode(p, it + G, mv_next, BV);
+    mv_next = meta_issue(p, it + 2 * G, lane);
+    if (cur.valid) {
+      item_ctx(c, cur);
+      c.A = cur.A;
+      stage_compute<kVerify, BV, TMAX>(st, raw, p, c, false, 0);
+    }
+    item_issue<BV, TMAX>(nxt, raw, land, p, c);
+    __syncthreads();
+    if (cur.valid) {
+      // Chunks of TMAX tokens (one chunk unless the row is longer than TMAX).
+      for (int c0 = 0; c0 < cur.T; c0 += TMAX) {
+        const int mm = (cur.T - c0) < TMAX ? (cur.T - c0) : TMAX;
+        if (c0 > 0) {
+          Raw<BV> more;
+          stage_load<kVerify, BV>(more, p, c, false, c0, mm);
+          __syncthreads();
+          stage_compute<kVerify, BV, TMAX>(st, more, p, c, false, c0);
+          __syncthreads();
         }
-        const uint2 kraw = *reinterpret_cast<const uint2*>(s.k + 4 * l32);
-        const uint2 graw = *reinterpret_cast<const uint2*>(s.g + 4 * l32);
-        float kx[4], gx[4];
-        unpack4(kraw, kx);
-        unpack4(graw, gx);
-        const float kn = sqrtf(reduce32(sum_sq4(kx)) + 1e-6f);
-        float4 kh, dk;
-        kh.x = kx[0] / kn; kh.y = kx[1] / kn; kh.z = kx[2] / kn; kh.w = kx[3] / kn;
-        dk.x = expf(gate_of(gx[0] + gb[0], A, p.has_lb, p.lower_bound));
-        dk.y = expf(gate_of(gx[1] + gb[1], A, p.has_lb, p.lower_bound));
-        dk.z = expf(gate_of(gx[2] + gb[2], A, p.has_lb, p.lower_bound));
-        dk.w = expf(gate_of(gx[3] + gb[3], A, p.has_lb, p.lower_bound));
-        *reinterpret_cast<float4*>(&st.kh[hw][4 * l32]) = kh;
-        *reinterpret_cast<float4*>(&st.dk[hw][4 * l32]) = dk;
-        if (!fold) {
-          const uint2 qraw = *reinterpret_cast<const uint2*>(s.q + 4 * l32);
-          float qx[4];
-          unpack4(qraw, qx);
-          const float qn = sqrtf(reduce32(sum_sq4(qx)) + 1e-6f);
-          float4 qh;
-          qh.x = (qx[0] / qn) * p.scale; qh.y = (qx[1] / qn) * p.scale;
-          qh.z = (qx[2] / qn) * p.scale; qh.w = (qx[3] / qn) * p.scale;
-          *reinterpret_cast<float4*>(&st.qh[hw][4 * l32]) = qh;
-        }
-        uint16_t vraw[VPL];
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) {
-          vraw[e] = s.v[tile * BV + l32 * VPL + e];
-          st.vt[hw][l32 * VPL + e] = bf16_to_f32(vraw[e]);
-        }
-        uint16_t braw = 0;
-        if (l32 == 0) {
-          braw = *s.b;
-          st.bt[hw] = 1.0f / (1.0f + expf(-bf16_to_f32(braw)));
-        }
-        // Records of the window (verify): raw inputs, first Q tokens only.
-        if ((MODE == kVerify || MODE == kDeferred) && !fold && j < p.Q) {
-          const long long base = ((long long)ri * H + head) * p.Q + j;
-          if (tile == 0) {
-            *reinterpret_cast<uint2*>(p.rk + base * KD + 4 * l32) = kraw;
-            *reinterpret_cast<uint2*>(p.rg + base * KD + 4 * l32) = graw;
-            if (l32 == 0) p.rb[base] = braw;
-          }
-#pragma unroll
-          for (int e = 0; e < VPL; ++e) p.rv[base * KD + tile * BV + l32 * VPL + e] = vraw[e];
-        }
-      }
-      __syncthreads();
-
-      // ---- token loop over the chunk -------------------------------------
-      for (int t = 0; t < m; ++t) {
-        float kh[16], dk[16];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float4 a = *reinterpret_cast<const float4*>(&st.kh[t][jj * 32 + p8 * 4]);
-          const float4 d = *reinterpret_cast<const float4*>(&st.dk[t][jj * 32 + p8 * 4]);
-          kh[4 * jj + 0] = a.x; kh[4 * jj + 1] = a.y; kh[4 * jj + 2] = a.z; kh[4 * jj + 3] = a.w;
-          dk[4 * jj + 0] = d.x; dk[4 * jj + 1] = d.y; dk[4 * jj + 2] = d.z; dk[4 * jj + 3] = d.w;
-        }
-        const float beta = st.bt[t];
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-          const int vloc = (rr * NWAVES + wave) * 8 + grp;
-          // decay the key channels
-#pragma unroll
-          for (int e = 0; e < 16; ++e) S[rr][e] = S[rr][e] * dk[e];
-          // S^T k^ for this value row
-          float acc[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float a = S[rr][4 * jj] * kh[4 * jj];
-            a = fmaf(S[rr][4 * jj + 1], kh[4 * jj + 1], a);
-            a = fmaf(S[rr][4 * jj + 2], kh[4 * jj + 2], a);
-            a = fmaf(S[rr][4 * jj + 3], kh[4 * jj + 3], a);
-            acc[jj] = a;
-          }
-          const float kv = reduce8((acc[0] + acc[1]) + (acc[2] + acc[3]));
-          const float u = beta * (st.vt[t][vloc] - kv);
-          // rank-1 update
-#pragma unroll
-          for (int e = 0; e < 16; ++e) S[rr][e] = fmaf(kh[e], u, S[rr][e]);
-        }
-        if (!fold) {
-          float qh[16];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float4 a = *reinterpret_cast<const float4*>(&st.qh[t][jj * 32 + p8 * 4]);
-            qh[4 * jj + 0] = a.x; qh[4 * jj + 1] = a.y; qh[4 * jj + 2] = a.z; qh[4 * jj + 3] = a.w;
-          }
-          const long long tok = (long long)bos + c0 + t;
-          uint16_t* orow = p.o + (tok * H + head) * KD + tile * BV;
-#pragma unroll
-          for (int rr = 0; rr < R; ++rr) {
-            float acc[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              float a = S[rr][4 * jj] * qh[4 * jj];
-              a = fmaf(S[rr][4 * jj + 1], qh[4 * jj + 1], a);
-              a = fmaf(S[rr][4 * jj + 2], qh[4 * jj + 2], a);
-              a = fmaf(S[rr][4 * jj + 3], qh[4 * jj + 3], a);
-              acc[jj] = a;
-            }
-            const float ov = reduce8((acc[0] + acc[1]) + (acc[2] + acc[3]));
-            if (p8 == 0) orow[(rr * NWAVES + wave) * 8 + grp] = f32_to_bf16(ov);
-          }
-        }
+        chunk_verify<R, BV, TMAX, TMAX>(S, st, p, c, mm, (long long)cur.bos + c0, c0 + mm < cur.T);
       }
     }
-    // The folded (deferred) or committed state goes back to the slot.
-    const bool store = (fold && MODE == kDeferred) || (MODE == kCommit) || (!fold && MODE == kRecurrent);
-    if (store) {
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr) {
-        const int vrow = tile * BV + (rr * NWAVES + wave) * 8 + grp;
-        float* dst = sbase + vrow * KD + p8 * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float4 x;
-          x.x = S[rr][4 * j + 0]; x.y = S[rr][4 * j + 1]; x.z = S[rr][4 * j + 2]; x.w = S[rr][4 * j + 3];
-          *reinterpret_cast<float4*>(dst + j * 32) = x;
-        }
-      }
-    }
+    it += G;
+    cur = nxt;
   }
 }
 
@@ -445,6 +845,7 @@ kda_status check_layer(const kda_layer* L) {
   if (!L || !L->a_log || !L->g_bias) return KDA_ERR_NULL;
   if (L->head_dim != KD) return KDA_ERR_UNSUPPORTED;
   if (L->num_heads <= 0) return KDA_ERR_SHAPE;
+  if (!aligned(L->g_bias, 16) || !aligned(L->a_log, 4)) return KDA_ERR_ALIGN;
   return KDA_OK;
 }
 
@@ -577,25 +978,94 @@ int tile_rows_for(long long pairs) {
   return 32;
 }
 
-template <int MODE, int R>
+template <int MODE, int R, int TMAX>
 kda_status launch_r(Params& p, hipStream_t stream) {
   p.tiles = KD / (32 * R);
   const long long blocks = (long long)p.num_rows * p.H * p.tiles;
   if (blocks > 0x7FFFFFFFLL) return KDA_ERR_SHAPE;
   p.total_blocks = (int)blocks;
   void* args[] = {&p};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel<MODE, R>),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel<MODE, R, TMAX>),
                                        dim3((unsigned)blocks), dim3(NTHREADS), args, 0, stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+// The verify modes keep 2 * R * TMAX dot products in registers: windows of
+// up to 4 tokens get a kernel with TMAX = 4 (fewer registers, more waves);
+// longer windows TMAX = 8 (CH). Longer rows still run, through the per-token
+// loop.
+template <int MODE, int TMAX>
+kda_status launch_t(Params& p, hipStream_t stream) {
+  switch (tile_rows_for((long long)p.num_rows * p.H)) {
+    case 32: return launch_r<MODE, 1, TMAX>(p, stream);
+    case 64: return launch_r<MODE, 2, TMAX>(p, stream);
+    default: return launch_r<MODE, 4, TMAX>(p, stream);
+  }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Workgroups of the persistent verify per compute unit: what fits at once
+// (registers, LDS), unless KDA_VERIFY_WG_PER_CU forces a number (read once).
+template <int R, int TMAX>
+int persistent_per_cu() {
+  static int n = 0;
+  if (n == 0) {
+    const char* env = getenv("KDA_VERIFY_WG_PER_CU");
+    if (env && atoi(env) > 0) {
+      n = atoi(env);
+    } else {
+      int b = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &b, reinterpret_cast<const void*>(&verify_persistent<R, TMAX>), NTHREADS, 0) != hipSuccess ||
+          b <= 0)
+        b = 1;
+      n = b;
+    }
+  }
+  return n;
+}
+
+template <int R, int TMAX>
+kda_status launch_verify_r(Params& p, hipStream_t stream) {
+  p.tiles = KD / (32 * R);
+  const long long items = (long long)p.num_rows * p.H * p.tiles;
+  if (items > 0x7FFFFFFFLL) return KDA_ERR_SHAPE;
+  p.total_blocks = (int)items;
+  const long long slots = (long long)device_cus() * persistent_per_cu<R, TMAX>();
+  const unsigned grid = (unsigned)(items < slots ? items : slots);
+  void* args[] = {&p};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_persistent<R, TMAX>),
+                                       dim3(grid), dim3(NTHREADS), args, 0, stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <int TMAX>
+kda_status launch_verify_t(Params& p, hipStream_t stream) {
+  switch (tile_rows_for((long long)p.num_rows * p.H)) {
+    case 32: return launch_verify_r<1, TMAX>(p, stream);
+    case 64: return launch_verify_r<2, TMAX>(p, stream);
+    default: return launch_verify_r<4, TMAX>(p, stream);
+  }
+}
+
 template <int MODE>
 kda_status launch(Params& p, hipStream_t stream) {
-  switch (tile_rows_for((long long)p.num_rows * p.H)) {
-    case 32: return launch_r<MODE, 1>(p, stream);
-    case 64: return launch_r<MODE, 2>(p, stream);
-    default: return launch_r<MODE, 4>(p, stream);
-  }
+  if (MODE == kVerify) return p.Q <= 4 ? launch_verify_t<4>(p, stream) : launch_verify_t<CH>(p, stream);
+  if ((MODE == kVerify || MODE == kDeferred) && p.Q <= 4) return launch_t<MODE, 4>(p, stream);
+  return launch_t<MODE, CH>(p, stream);
 }
 
 }  // namespace
