@@ -20,6 +20,9 @@ bounded sample of the same workload).
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -53,6 +56,80 @@ def algorithmic_bytes(T, n_commit, valid, H):
     return float(verify), float(commit)
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_speculative_kda_amd", "csrc", "kda.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 30   # the plain copy timed below: 1 GiB read + 1 GiB written
+
+
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def kernel_key(name: str) -> str:
+    """Library kernel -> call name (by template mode); others keep their name."""
+    if "verify_persistent" in name or "kda_kernel<1," in name:
+        return "kda_verify"
+    for mode, call in (("0", "kda_recurrent"), ("2", "kda_commit"), ("3", "kda_verify_deferred")):
+        if f"kda_kernel<{mode}," in name:
+            return call
+    return name
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str) -> dict:
+    """Per-dispatch HBM traffic of each library kernel from two rocprofv3
+    --pmc runs of this benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch). Each counter is calibrated on the plain 1 GiB copy that the
+    benchmark times: its dispatches write exactly 1 GiB, so
+    factor = 1 GiB / (what the counter reads for them)."""
+    def load(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_kib = COPY_BYTES / 1024
+    # The two runs dispatch the same sequence; pair the copies by dispatch id.
+    copy_ids = {i for i, k, v in write if "copyBuffer" in k and abs(v - copy_kib) < 0.01 * copy_kib}
+    copy_w = [v for i, k, v in write if i in copy_ids]
+    copy_f = [v for i, k, v in fetch if i in copy_ids and "copyBuffer" in k]
+    if not copy_w or not copy_f:
+        raise SystemExit("no 1 GiB copy dispatches found to calibrate the counters")
+    f_scale = copy_kib / float(np.median(copy_f))
+    w_scale = copy_kib / float(np.median(copy_w))
+    out = {"source_sha256": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_fetch_kib": float(np.median(copy_f)), "copy_write_kib": float(np.median(copy_w)),
+           "kernels": {}}
+    by = {}
+    for _, name, v in fetch:
+        by.setdefault(kernel_key(name), {}).setdefault("fetch", []).append(v)
+    for _, name, v in write:
+        by.setdefault(kernel_key(name), {}).setdefault("write", []).append(v)
+    for key, d in by.items():
+        if not key.startswith("kda_") or "fetch" not in d or "write" not in d:
+            continue
+        fk, wk = float(np.median(d["fetch"])), float(np.median(d["write"]))
+        out["kernels"][key] = {"fetch_kib": fk, "write_kib": wk, "dispatches": len(d["fetch"]),
+                               "traffic_bytes": (fk * f_scale + wk * w_scale) * 1024}
+    return out
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k["traffic_bytes"]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -64,11 +141,20 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU sample until this much wall time is spent")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        out = summarize_pmc(*args.summarize_pmc)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out, indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path shards by requests and heads with "
               "no exchange, and no multi-GPU run is part of this build.", file=sys.stderr)
@@ -219,7 +305,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": kernels[dom]["gbs"] / PEAK_HBM_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(dom),
         },
         "kernels": kernels,
         "step_gbs": (vbytes + cbytes) / (ms_step * 1e6),

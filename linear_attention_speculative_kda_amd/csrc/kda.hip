@@ -957,12 +957,14 @@ void set_records(Params& p, const kda_records* r) {
   p.Q = r->window;
 }
 
-// Rows of the state tile per workgroup: 32 * R. One workgroup per (row, head)
-// (128 rows) when there are enough (row, head) pairs to fill the chip;
-// smaller batches split V into 2 or 4 tiles for more workgroups. The per-row
-// arithmetic does not depend on the tile size. KDA_TILE_ROWS in {32, 64, 128}
-// forces a size (read once).
-int tile_rows_for(long long pairs) {
+// Rows of the state tile per workgroup: 32 * R (measured on MI355X at
+// H = 32, K = V = 128). The commit and the plain recurrence keep the
+// workgroups short and numerous (32 rows: four tiles per head); the verify
+// calls carry the per-head staging and coefficients, which 64-row tiles
+// share better. Small batches use 32 rows for more workgroups. The per-row
+// arithmetic does not depend on the tile size. KDA_TILE_ROWS in
+// {32, 64, 128} forces a size (read once).
+int tile_rows_for(int mode, long long pairs) {
   static int forced = -2;
   if (forced == -2) {
     forced = -1;
@@ -973,9 +975,8 @@ int tile_rows_for(long long pairs) {
     }
   }
   if (forced > 0) return forced;
-  if (pairs >= 2048) return 128;
-  if (pairs >= 1024) return 64;
-  return 32;
+  if (mode == kCommit || mode == kRecurrent) return 32;
+  return pairs >= 512 ? 64 : 32;
 }
 
 template <int MODE, int R, int TMAX>
@@ -996,7 +997,7 @@ kda_status launch_r(Params& p, hipStream_t stream) {
 // loop.
 template <int MODE, int TMAX>
 kda_status launch_t(Params& p, hipStream_t stream) {
-  switch (tile_rows_for((long long)p.num_rows * p.H)) {
+  switch (tile_rows_for(MODE, (long long)p.num_rows * p.H)) {
     case 32: return launch_r<MODE, 1, TMAX>(p, stream);
     case 64: return launch_r<MODE, 2, TMAX>(p, stream);
     default: return launch_r<MODE, 4, TMAX>(p, stream);
@@ -1054,7 +1055,7 @@ kda_status launch_verify_r(Params& p, hipStream_t stream) {
 
 template <int TMAX>
 kda_status launch_verify_t(Params& p, hipStream_t stream) {
-  switch (tile_rows_for((long long)p.num_rows * p.H)) {
+  switch (tile_rows_for(kVerify, (long long)p.num_rows * p.H)) {
     case 32: return launch_verify_r<1, TMAX>(p, stream);
     case 64: return launch_verify_r<2, TMAX>(p, stream);
     default: return launch_verify_r<4, TMAX>(p, stream);
