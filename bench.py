@@ -68,7 +68,7 @@ def source_hash() -> str:
 
 def kernel_key(name: str) -> str:
     """Library kernel -> call name (by template mode); others keep their name."""
-    if "verify_persistent" in name or "kda_kernel<1," in name:
+    if "kda_kernel<1," in name:
         return "kda_verify"
     for mode, call in (("0", "kda_recurrent"), ("2", "kda_commit"), ("3", "kda_verify_deferred")):
         if f"kda_kernel<{mode}," in name:

@@ -175,6 +175,29 @@ __device__ __forceinline__ float dot4(const float a[4], const float b[4]) {
   return s;
 }
 
+// Workgroup barrier for data handed between waves through LDS.
+// __syncthreads() is a workgroup release/acquire fence plus s_barrier, and
+// the fence waits for every outstanding global load and store of the wave
+// (vmcnt 0): a workgroup that has just issued its state-tile loads would
+// wait for the whole tile at its first barrier, before the token staging
+// that does not need it. LDS data only needs the wave's own LDS operations
+// finished (lgkmcnt 0) before the barrier; no kernel here hands global
+// memory between the waves of a workgroup.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A load of a workgroup-uniform value that this kernel never writes, through
+// the constant address space so that it becomes a scalar load. A plain load
+// may be emitted as a vector load when the kernel also stores to global
+// memory, and its first use would then wait for every vector load issued
+// before it.
+template <class T>
+__device__ __forceinline__ T scalar_load(const T* ptr) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(
+      reinterpret_cast<uintptr_t>(ptr));
+}
+
 // LDS staging area for one chunk of up to NT tokens.
 template <int BV, int NT>
 struct Stage {
@@ -307,12 +330,30 @@ __device__ __forceinline__ void stage_load(Raw<BV>& x, const Params& p, const Ct
   x.b = (l32 == 0) ? *b : (uint16_t)0;
 }
 
+// Write a staged window token's raw inputs to its record row (the first Q
+// tokens of the row; the tile-0 workgroup writes k, g and beta, every tile
+// its slice of v).
+template <int BV>
+__device__ __forceinline__ void store_records(const Raw<BV>& x, const Params& p, const Ctx& c, int c0) {
+  constexpr int VPL = BV / 32;
+  const int l32 = c.l32, j = c0 + c.hw;
+  if (!x.active || j >= p.Q) return;
+  const long long base = ((long long)c.ri * c.H + c.head) * p.Q + j;
+  if (c.tile == 0) {
+    *reinterpret_cast<uint2*>(p.rk + base * KD + 4 * l32) = x.k;
+    *reinterpret_cast<uint2*>(p.rg + base * KD + 4 * l32) = x.g;
+    if (l32 == 0) p.rb[base] = x.b;
+  }
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) p.rv[base * KD + c.tile * BV + l32 * VPL + e] = x.v[e];
+}
+
 // Turn the loaded raw inputs into the per-token vectors in LDS; for window
-// tokens of the verify modes also write the raw inputs to the records (first
-// Q tokens only).
+// tokens of the verify modes also write the raw inputs to the records
+// unless `records` is false (the caller then calls store_records itself).
 template <int MODE, int BV, int NT>
 __device__ __forceinline__ void stage_compute(Stage<BV, NT>& st, const Raw<BV>& x, const Params& p,
-                                              const Ctx& c, bool fold, int c0) {
+                                              const Ctx& c, bool fold, int c0, bool records = true) {
   constexpr int VPL = BV / 32;
   if (!x.active) return;
   const int hw = c.hw, l32 = c.l32, j = c0 + hw;
@@ -340,16 +381,7 @@ __device__ __forceinline__ void stage_compute(Stage<BV, NT>& st, const Raw<BV>& 
 #pragma unroll
   for (int e = 0; e < VPL; ++e) st.vt[hw][l32 * VPL + e] = bf16_to_f32(x.v[e]);
   if (l32 == 0) st.bt[hw] = sigmoid_hw(bf16_to_f32(x.b));
-  if ((MODE == kVerify || MODE == kDeferred) && !fold && j < p.Q) {
-    const long long base = ((long long)c.ri * c.H + c.head) * p.Q + j;
-    if (c.tile == 0) {
-      *reinterpret_cast<uint2*>(p.rk + base * KD + 4 * l32) = x.k;
-      *reinterpret_cast<uint2*>(p.rg + base * KD + 4 * l32) = x.g;
-      if (l32 == 0) p.rb[base] = x.b;
-    }
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) p.rv[base * KD + c.tile * BV + l32 * VPL + e] = x.v[e];
-  }
+  if ((MODE == kVerify || MODE == kDeferred) && !fold && records) store_records<BV>(x, p, c, c0);
 }
 
 // The per-token recurrence over m staged tokens, state in registers. With
@@ -386,8 +418,9 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
   }
 }
 
-// Verify of a chunk of m <= TMAX staged tokens from the state in registers.
-// Unrolling the recurrence from the chunk's start state S0:
+// Verify of a chunk of m <= TMAX staged tokens (the chunked form) from the
+// state S0 in registers, without stepping the state token by token.
+// Unrolling the recurrence from S0:
 //   a_t = (Gamma_t S0)^T k^_t,  b_t = (Gamma_t S0)^T q^_t
 //   u_t = beta_t (v_t - a_t - sum_{s<t} M[t][s] u_s)
 //   o_t = b_t + sum_{s<=t} N[t][s] u_s
@@ -395,11 +428,11 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
 // with 2m dot products per value row instead of 4m passes over it. With
 // `more`, the state is advanced to the chunk's end for the next chunk:
 //   S_m = Gamma_m S0 + sum_s P(s,m) k^_s u_s^T.
-// Outputs go to o[tok0 + t].
-template <int R, int BV, int TMAX, int NT>
-__device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, NT>& st,
-                                             const Params& p, const Ctx& c, int T,
-                                             long long tok0, bool more) {
+//
+// coef_phase: the per-chunk vectors and coefficients, from the staged k^,
+// q^, exp(g), by 256 threads (c.tid 0..255; c.hw and c.l32 relative to them).
+template <int BV, int TMAX, int NT>
+__device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c, int T, bool more) {
   // Decayed vectors: threads 0..127, one key channel each (all of the
   // channel's staged values are read first, then a short product chain).
   if (c.tid < KD) {
@@ -481,10 +514,14 @@ __device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, N
       }
     }
   }
-  __syncthreads();
+}
 
-  // 2T dot products per value row against the chunk's start state.
-  float a[R][TMAX], b[R][TMAX];
+// chunk_dots: the 2T dot products per value row against the chunk's start
+// state (a_t with Gamma_t k^_t, b_t with Gamma_t q^_t).
+template <int R, int BV, int TMAX, int NT>
+__device__ __forceinline__ void chunk_dots(const float (&S)[R][16], const StageChunk<BV, NT>& st,
+                                           const Ctx& c, int T, float (&a)[R][TMAX],
+                                           float (&b)[R][TMAX]) {
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {
     if (t < T) {
@@ -497,8 +534,16 @@ __device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, N
       for (int rr = 0; rr < R; ++rr) b[rr][t] = row_dot(S[rr], v16);
     }
   }
-  // The T x T triangular recurrence per value row; lane p8 of the group
-  // stores token p8's output.
+}
+
+// chunk_recur: the T x T triangular recurrence per value row, the outputs
+// (lane p8 of the group stores token p8's output, to o[tok0 + p8]) and, with
+// `more`, the state at the chunk's end.
+template <int R, int BV, int TMAX, int NT>
+__device__ __forceinline__ void chunk_recur(float (&S)[R][16], const StageChunk<BV, NT>& st,
+                                            const Params& p, const Ctx& c, int T, long long tok0,
+                                            bool more, const float (&a)[R][TMAX],
+                                            const float (&b)[R][TMAX]) {
   float u[R][TMAX];
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
@@ -538,6 +583,17 @@ __device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, N
       }
     }
   }
+}
+
+template <int R, int BV, int TMAX, int NT>
+__device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, NT>& st,
+                                             const Params& p, const Ctx& c, int T,
+                                             long long tok0, bool more) {
+  coef_phase<BV, TMAX, NT>(st, c, T, more);
+  lds_barrier();
+  float a[R][TMAX], b[R][TMAX];
+  chunk_dots<R, BV, TMAX, NT>(S, st, c, T, a, b);
+  chunk_recur<R, BV, TMAX, NT>(S, st, p, c, T, tok0, more, a, b);
 }
 
 // ------------------------------------------------------------------ kernel --
@@ -606,9 +662,31 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
     nmain = T;
   }
   if (!slot_ok || (nfold == 0 && nmain == 0)) return;
-  c.A = exp_hw(p.a_log[c.head]);
+  c.A = exp_hw(scalar_load(p.a_log + c.head));
   float* sbase = p.state + (long long)slot * p.slot_stride + (long long)c.head * KD * KD;
   const bool chunk = kChunk && nmain <= TMAX;
+
+  // Verify of a window that fits one chunk: straight-line code from the
+  // loads to the outputs. A control-flow join between the state loads and
+  // their first use lets the compiler copy the state registers there, which
+  // waits for the whole tile before the token staging can start.
+  if constexpr (MODE == kVerify) {
+    if (chunk) {
+      Raw<BV> raw;
+      stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
+      __builtin_amdgcn_sched_barrier(0);
+      float S[R][16];
+      load_tile<R, BV>(S, sbase, c);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0, false);
+      lds_barrier();
+      chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos, false);
+      // the records last: stores issued behind the state loads would make
+      // later register reuse wait for those loads
+      store_records<BV>(raw, p, c, 0);
+      return;
+    }
+  }
 
   // The first chunk's token loads go out before the state tile's: loads
   // complete in issue order, so the staging math then waits for its own
@@ -627,9 +705,9 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
     for (int c0 = 0; c0 < nfold; c0 += CH) {
       const int m = (nfold - c0) < CH ? (nfold - c0) : CH;
       if (c0 > 0) stage_load<MODE, BV>(raw, p, c, true, c0, m);
-      __syncthreads();  // the previous chunk is consumed
+      lds_barrier();  // the previous chunk is consumed
       stage_compute<MODE, BV, CH>(st, raw, p, c, true, c0);
-      __syncthreads();
+      lds_barrier();
       seq_tokens<R, BV, CH>(S, st, p, c, m, false, 0);
     }
     store_tile<R, BV>(S, sbase, c);
@@ -640,9 +718,9 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
   if (nmain > 0) {
     if constexpr (kChunk) {
       if (chunk) {
-        __syncthreads();
+        lds_barrier();
         stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0);
-        __syncthreads();
+        lds_barrier();
         chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos, false);
         return;
       }
@@ -650,173 +728,12 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
     for (int c0 = 0; c0 < nmain; c0 += CH) {
       const int m = (nmain - c0) < CH ? (nmain - c0) : CH;
       if (c0 > 0) stage_load<MODE, BV>(raw, p, c, false, c0, m);
-      __syncthreads();
+      lds_barrier();
       stage_compute<MODE, BV, CH>(st, raw, p, c, false, c0);
-      __syncthreads();
+      lds_barrier();
       seq_tokens<R, BV, CH>(S, st, p, c, m, true, (long long)bos + c0);
     }
     if (MODE == kRecurrent) store_tile<R, BV>(S, sbase, c);
-  }
-}
-
-// ------------------------------------------------------- persistent verify --
-//
-// kda_verify reads each 64 KiB state once and writes no state, so the state
-// loads must overlap the per-head math for the kernel to run at the speed of
-// HBM. A fixed grid (as many workgroups as fit on the chip) walks the
-// (row, head, tile) items with a stride. Each item's state tile is streamed
-// straight into an LDS landing buffer (global_load_lds_dwordx4: each lane's
-// 16 bytes land at base + 16 * lane, one KiB per wave instruction) while the
-// previous item is computed; at the start of an item the tile moves from LDS
-// into registers and the buffer is refilled with the next item's tile.
-
-struct Item {
-  int row, head, tile, bos, T, ri;
-  float A;                  // exp(A_log[head])
-  const float* tile_base;   // first value row of the item's state tile
-  bool valid;
-};
-
-// An item's metadata is fetched with one vector load per lane (lane 0:
-// cu_seqlens[row], 1: cu_seqlens[row+1], 2: the slot, 3: the record row,
-// 4: A_log[head]) two items ahead, so that it never waits on scalar loads,
-// which share a counter with LDS.
-__device__ __forceinline__ int meta_issue(const Params& p, int it, int lane) {
-  if (it >= p.total_blocks) return 0;
-  const int rh = it / p.tiles;
-  const int head = rh % p.H;
-  const int row = rh / p.H;
-  const int* src = p.cu + row;
-  if (lane == 1) src = p.cu + row + 1;
-  if (lane == 2) src = p.slots + row;
-  if (lane == 3 && p.record_rows) src = p.record_rows + row;
-  if (lane == 4) src = reinterpret_cast<const int*>(p.a_log) + head;
-  const int v = *src;
-  return (lane == 3 && !p.record_rows) ? row : v;
-}
-
-__device__ __forceinline__ Item item_decode(const Params& p, int it, int mv, int BV) {
-  Item m;
-  m.valid = false;
-  m.T = 0;
-  m.A = 1.0f;
-  m.tile_base = nullptr;
-  if (it >= p.total_blocks) return m;
-  m.tile = it % p.tiles;
-  const int rh = it / p.tiles;
-  m.head = rh % p.H;
-  m.row = rh / p.H;
-  const int bos = __builtin_amdgcn_readlane(mv, 0);
-  const int eos = __builtin_amdgcn_readlane(mv, 1);
-  const int slot = __builtin_amdgcn_readlane(mv, 2);
-  const int r = __builtin_amdgcn_readlane(mv, 3);
-  m.A = exp_hw(__int_as_float(__builtin_amdgcn_readlane(mv, 4)));
-  int T = eos - bos;
-  if (bos < 0 || T < 0 || eos > p.num_tokens) T = 0;
-  m.bos = bos;
-  m.T = T;
-  m.ri = (r >= 0 && r < p.rec_rows) ? r + 1 : 0;
-  m.valid = slot > 0 && slot < p.num_slots && T > 0;
-  if (m.valid)
-    m.tile_base = p.state + (long long)slot * p.slot_stride + (long long)m.head * KD * KD +
-                  (long long)m.tile * BV * KD;
-  return m;
-}
-
-__device__ __forceinline__ void item_ctx(Ctx& c, const Item& m) {
-  c.bos = m.bos;
-  c.ri = m.ri;
-  c.head = m.head;
-  c.tile = m.tile;
-}
-
-// Issue an item's loads: the first chunk of token inputs into registers, the
-// state tile into the LDS landing buffer (rows 2g and 2g+1 per instruction).
-template <int BV, int TMAX>
-__device__ __forceinline__ void item_issue(const Item& m, Raw<BV>& raw, float* land,
-                                           const Params& p, Ctx c) {
-  if (!m.valid) return;
-  item_ctx(c, m);
-  stage_load<kVerify, BV>(raw, p, c, false, 0, m.T < TMAX ? m.T : TMAX);
-  constexpr int NI = BV / (2 * NWAVES);   // landing instructions per wave
-  const int lane = c.tid & 63;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int g = c.wave * NI + i;
-    const float* src = m.tile_base + 2 * g * KD + lane * 4;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(land + 2 * g * KD),
-                                     16, 0, 0);
-  }
-}
-
-template <int R, int BV>
-__device__ __forceinline__ void land_to_regs(float (&S)[R][16], const float* land, const Ctx& c) {
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const float* src = land + row_in_tile(rr, c) * KD + c.p8 * 4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 x = *reinterpret_cast<const float4*>(src + j * 32);
-      S[rr][4 * j + 0] = x.x; S[rr][4 * j + 1] = x.y; S[rr][4 * j + 2] = x.z; S[rr][4 * j + 3] = x.w;
-    }
-  }
-}
-
-template <int R, int TMAX>
-__global__ __launch_bounds__(NTHREADS) void verify_persistent(Params p) {
-  constexpr int BV = R * NWAVES * 8;
-  __shared__ StageChunk<BV, TMAX> st;
-  __shared__ __attribute__((aligned(16))) float land[BV * KD];
-  Ctx c;
-  c.tid = threadIdx.x;
-  c.wave = c.tid >> 6;
-  c.p8 = c.tid & 7;
-  c.grp = (c.tid & 63) >> 3;
-  c.hw = c.tid >> 5;
-  c.l32 = c.tid & 31;
-  c.H = p.H;
-
-  const int G = gridDim.x;
-  const int lane = c.tid & 63;
-  int it = blockIdx.x;
-  Raw<BV> raw;
-  Item cur = item_decode(p, it, meta_issue(p, it, lane), BV);
-  int mv_next = meta_issue(p, it + G, lane);
-  item_issue<BV, TMAX>(cur, raw, land, p, c);
-  float S[R][16];
-  while (it < p.total_blocks) {
-    // The item's tile and inputs have landed (this also drains the previous
-    // item's stores, long done by now).
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (cur.valid) land_to_regs<R, BV>(S, land, c);
-    __syncthreads();   // the landing buffer and the staging area are free
-    const Item nxt = item_decode(p, it + G, mv_next, BV);
-    mv_next = meta_issue(p, it + 2 * G, lane);
-    if (cur.valid) {
-      item_ctx(c, cur);
-      c.A = cur.A;
-      stage_compute<kVerify, BV, TMAX>(st, raw, p, c, false, 0);
-    }
-    item_issue<BV, TMAX>(nxt, raw, land, p, c);
-    __syncthreads();
-    if (cur.valid) {
-      // Chunks of TMAX tokens (one chunk unless the row is longer than TMAX).
-      for (int c0 = 0; c0 < cur.T; c0 += TMAX) {
-        const int mm = (cur.T - c0) < TMAX ? (cur.T - c0) : TMAX;
-        if (c0 > 0) {
-          Raw<BV> more;
-          stage_load<kVerify, BV>(more, p, c, false, c0, mm);
-          __syncthreads();
-          stage_compute<kVerify, BV, TMAX>(st, more, p, c, false, c0);
-          __syncthreads();
-        }
-        chunk_verify<R, BV, TMAX, TMAX>(S, st, p, c, mm, (long long)cur.bos + c0, c0 + mm < cur.T);
-      }
-    }
-    it += G;
-    cur = nxt;
   }
 }
 
@@ -959,9 +876,10 @@ void set_records(Params& p, const kda_records* r) {
 
 // Rows of the state tile per workgroup: 32 * R (measured on MI355X at
 // H = 32, K = V = 128). The commit and the plain recurrence keep the
-// workgroups short and numerous (32 rows: four tiles per head); the verify
-// calls carry the per-head staging and coefficients, which 64-row tiles
-// share better. Small batches use 32 rows for more workgroups. The per-row
+// workgroups short and numerous (32 rows: four tiles per head). The verify
+// calls repeat the per-head token staging and coefficients in every tile,
+// so larger tiles pay off once there are enough (row, head) pairs to fill
+// the chip: 128 rows from 4096 pairs, 64 from 512, else 32. The per-row
 // arithmetic does not depend on the tile size. KDA_TILE_ROWS in
 // {32, 64, 128} forces a size (read once).
 int tile_rows_for(int mode, long long pairs) {
@@ -976,6 +894,7 @@ int tile_rows_for(int mode, long long pairs) {
   }
   if (forced > 0) return forced;
   if (mode == kCommit || mode == kRecurrent) return 32;
+  if (mode == kVerify && pairs >= 4096) return 128;
   return pairs >= 512 ? 64 : 32;
 }
 
@@ -1004,67 +923,8 @@ kda_status launch_t(Params& p, hipStream_t stream) {
   }
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
-// Workgroups of the persistent verify per compute unit: what fits at once
-// (registers, LDS), unless KDA_VERIFY_WG_PER_CU forces a number (read once).
-template <int R, int TMAX>
-int persistent_per_cu() {
-  static int n = 0;
-  if (n == 0) {
-    const char* env = getenv("KDA_VERIFY_WG_PER_CU");
-    if (env && atoi(env) > 0) {
-      n = atoi(env);
-    } else {
-      int b = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &b, reinterpret_cast<const void*>(&verify_persistent<R, TMAX>), NTHREADS, 0) != hipSuccess ||
-          b <= 0)
-        b = 1;
-      n = b;
-    }
-  }
-  return n;
-}
-
-template <int R, int TMAX>
-kda_status launch_verify_r(Params& p, hipStream_t stream) {
-  p.tiles = KD / (32 * R);
-  const long long items = (long long)p.num_rows * p.H * p.tiles;
-  if (items > 0x7FFFFFFFLL) return KDA_ERR_SHAPE;
-  p.total_blocks = (int)items;
-  const long long slots = (long long)device_cus() * persistent_per_cu<R, TMAX>();
-  const unsigned grid = (unsigned)(items < slots ? items : slots);
-  void* args[] = {&p};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_persistent<R, TMAX>),
-                                       dim3(grid), dim3(NTHREADS), args, 0, stream);
-  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
-}
-
-template <int TMAX>
-kda_status launch_verify_t(Params& p, hipStream_t stream) {
-  switch (tile_rows_for(kVerify, (long long)p.num_rows * p.H)) {
-    case 32: return launch_verify_r<1, TMAX>(p, stream);
-    case 64: return launch_verify_r<2, TMAX>(p, stream);
-    default: return launch_verify_r<4, TMAX>(p, stream);
-  }
-}
-
 template <int MODE>
 kda_status launch(Params& p, hipStream_t stream) {
-  if (MODE == kVerify) return p.Q <= 4 ? launch_verify_t<4>(p, stream) : launch_verify_t<CH>(p, stream);
   if ((MODE == kVerify || MODE == kDeferred) && p.Q <= 4) return launch_t<MODE, 4>(p, stream);
   return launch_t<MODE, CH>(p, stream);
 }
