@@ -263,6 +263,25 @@ def main():
         kinfo["frac_of_peak"] = kinfo["gbs"] / PEAK_HBM_GBS
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
 
+    # ---- context: kda_verify without a commit before it. In the step, the
+    # previous commit's 128 MiB of new state is still being written back from
+    # the MALL while the next verify streams its checkpoints, so the verify's
+    # event time carries part of the commit's writes.
+    ev_iso = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(len(sets)):
+        verify(sets[i])
+    torch.cuda.synchronize()
+    for i in range(K):
+        s = sets[i % len(sets)]
+        ev_iso[i][0].record(stream)
+        verify(s)
+        ev_iso[i][1].record(stream)
+    torch.cuda.synchronize()
+    ti = np.array([a.elapsed_time(b) for a, b in ev_iso])
+    verify_isolated = dict(avg_us=float(ti.mean()) * 1e3, median_us=float(np.median(ti)) * 1e3,
+                           gbs=vbytes / (float(ti.mean()) * 1e6))
+    verify_isolated["frac_of_peak"] = verify_isolated["gbs"] / PEAK_HBM_GBS
+
     # ---- achievable copy bandwidth on this GPU (context for the peak)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
     dst = torch.empty_like(src)
@@ -308,6 +327,7 @@ def main():
             "traffic": measured_traffic(dom),
         },
         "kernels": kernels,
+        "kda_verify_without_preceding_commit": verify_isolated,
         "step_gbs": (vbytes + cbytes) / (ms_step * 1e6),
         "step_frac_of_peak": (vbytes + cbytes) / (ms_step * 1e6) / PEAK_HBM_GBS,
         "commit_tokens_per_s": tok_commit / (c_ms * 1e-3),
