@@ -282,6 +282,39 @@ def main():
                            gbs=vbytes / (float(ti.mean()) * 1e6))
     verify_isolated["frac_of_peak"] = verify_isolated["gbs"] / PEAK_HBM_GBS
 
+    # ---- the step as a serving loop runs it: captured in a HIP graph (one
+    # graph per input set: verify then commit), replayed for exactly K steps.
+    # The eager loop above gives the per-kernel times; this one the step.
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for s in sets:
+            kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
+                           s["rec"], s["o"], stream=side)
+            kda.kda_commit(layer, cu, s["pool"], si, s["rec"], nacc, stream=side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    for s in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
+                           s["rec"], s["o"], stream=cap)
+            kda.kda_commit(layer, cu, s["pool"], si, s["rec"], nacc, stream=cap)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    g_start = torch.cuda.Event(enable_timing=True)
+    g_end = torch.cuda.Event(enable_timing=True)
+    g_start.record(stream)
+    for i in range(K):
+        graphs[i % len(graphs)].replay()
+    g_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step_graph = g_start.elapsed_time(g_end) / K
+
     # ---- achievable copy bandwidth on this GPU (context for the peak)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
     dst = torch.empty_like(src)
@@ -299,12 +332,12 @@ def main():
 
     result = {
         "metric": "KDA verify+commit tokens/s and achieved HBM GB/s vs peak (B=64,H=32,T=4)",
-        "value": tok_verify / (ms_step * 1e-3),
+        "value": tok_verify / (ms_step_graph * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": ms_step_graph,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -328,8 +361,12 @@ def main():
         },
         "kernels": kernels,
         "kda_verify_without_preceding_commit": verify_isolated,
-        "step_gbs": (vbytes + cbytes) / (ms_step * 1e6),
-        "step_frac_of_peak": (vbytes + cbytes) / (ms_step * 1e6) / PEAK_HBM_GBS,
+        "step_gbs": (vbytes + cbytes) / (ms_step_graph * 1e6),
+        "step_frac_of_peak": (vbytes + cbytes) / (ms_step_graph * 1e6) / PEAK_HBM_GBS,
+        "step_timing": "HIP graph replay (verify + commit per step); per-kernel times from "
+                       "HIP events around eager launches",
+        "ms_per_step_eager": ms_step,
+        "value_eager": tok_verify / (ms_step * 1e-3),
         "commit_tokens_per_s": tok_commit / (c_ms * 1e-3),
         "verify_tokens_per_s": tok_verify / (v_ms * 1e-3),
         "copy_gbs_measured": copy_gbs,
