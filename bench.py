@@ -135,7 +135,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "deep", "ragged"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "deep", "ragged", "deferred"])
     ap.add_argument("--sets", type=int, default=6, help="independent input copies rotated")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the CPU oracle sample")
@@ -166,6 +166,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "deferred":
+        print(json.dumps(deferred_leg(args, torch, kda, dev)), flush=True)
+        return
     batch = make_batch(args.workload)
     B, H, Q = batch.num_rows, batch.H, batch.Q
     T = batch.seq_lens()
@@ -376,6 +379,165 @@ def main():
         result["cpu_baseline"] = cpu_baseline(batch, args.cpu_rows, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def deferred_bytes(T, n_prev, eager_prev, n_now, eager_now, valid, H):
+    """Bytes of one layer-step of each flow (each counted once).
+
+    eager:    verify (65,536 + 2,052 T) + commit (131,072 + 770 n' when n' > 0).
+    deferred: kda_verify_deferred folds the previous step's pending p records
+              (p = n' of the previous step unless that row was eager): 65,536
+              + [p > 0] 65,536 + 770 p + 2,052 T; then kda_commit writes pending
+              and commits the eager rows now: 131,072 + 770 n' for those."""
+    T = np.asarray(T)[valid]
+    p = np.where(np.asarray(eager_prev)[valid] != 0, 0, np.asarray(n_prev)[valid])
+    n = np.asarray(n_now)[valid]
+    e = np.asarray(eager_now)[valid] != 0
+    per_tok = TOKEN_IN_BYTES + OUT_BYTES + REC_BYTES
+    verify = H * np.sum(STATE_BYTES + per_tok * T)
+    commit = H * np.sum(np.where(n > 0, 2 * STATE_BYTES + REC_BYTES * n, 0))
+    vdef = H * np.sum(STATE_BYTES + np.where(p > 0, STATE_BYTES + REC_BYTES * p, 0) + per_tok * T)
+    cdef = H * np.sum(np.where(e & (n > 0), 2 * STATE_BYTES + REC_BYTES * n, 0))
+    return float(verify + commit), float(vdef), float(cdef)
+
+
+def deferred_leg(args, torch, kda, dev):
+    """Many layers, many steps: the eager flow (kda_verify for every layer,
+    then kda_commit for every layer) against the deferred flow
+    (kda_verify_deferred for every layer, folding the previous step's pending
+    commit, then kda_commit in deferred mode, which records pending counts and
+    commits the eager rows now). B=512, H=32, T=Q=4, 8 layers, each with its
+    own pool of 513 slots (1 GiB) and its own records. The checkpoints are
+    N(0, 0.02) drawn on the device with torch's seeded generator (the same
+    distribution as the parity recipe, drawn faster); tokens are the
+    workload's per-layer draws of step 0, reused every step."""
+    from workloads import make_deferred
+    run = make_deferred()
+    B, H, Q, T, L = run.B, run.H, run.Q, run.T, run.layers
+    ntok = B * T
+    hk = H * 128
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    def up_bf16(bits):
+        return up(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(run.seed)
+    si, rr, cu = up(run.state_indices), up(run.record_rows), up(run.cu_seqlens)
+    layers, pools, toks, recs = [], [], [], []
+    for l in range(L):
+        p = run.params[l]
+        layers.append(kda.Layer(a_log=up(p.a_log), g_bias=up(p.g_bias), scale=run.scale,
+                                lower_bound=run.lower_bound))
+        pool = torch.zeros((run.num_slots, H, 128, 128), dtype=torch.float32, device=dev)
+        pool[1:].normal_(0.0, 0.02, generator=gen)
+        pools.append(pool)
+        t = run.tokens(l, 0)
+        qkv = up_bf16(t.qkv)
+        toks.append((qkv[:, :hk].view(ntok, H, 128), qkv[:, hk:2 * hk].view(ntok, H, 128),
+                     qkv[:, 2 * hk:].view(ntok, H, 128), up_bf16(t.g), up_bf16(t.beta), qkv))
+        recs.append([kda.allocate_records(B, H, Q, dev), kda.allocate_records(B, H, Q, dev)])
+    o = torch.empty((ntok, H, 128), dtype=torch.bfloat16, device=dev)
+    pending = torch.zeros(B, dtype=torch.int32, device=dev)
+    S = run.steps
+    nacc = [up(run.num_accepted(s)) for s in range(S)]
+    eag = [up(run.eager(s)) for s in range(S)]
+    stream = torch.cuda.current_stream()
+
+    def eager_step(s, ev=None):
+        for l in range(L):
+            kda.kda_verify(layers[l], *toks[l][:5], cu, pools[l], si, recs[l][0], o,
+                           record_rows=rr, stream=stream)
+        for l in range(L):
+            kda.kda_commit(layers[l], cu, pools[l], si, recs[l][0], nacc[s % S], record_rows=rr,
+                           stream=stream)
+
+    def deferred_step(s, ev=None):
+        cur = s % 2
+        for l in range(L):
+            if ev is not None:
+                ev[l][0].record(stream)
+            kda.kda_verify_deferred(layers[l], *toks[l][:5], cu, pools[l], si, recs[l][1 - cur],
+                                    pending, recs[l][cur], o, record_rows=rr, stream=stream)
+            if ev is not None:
+                ev[l][1].record(stream)
+        for l in range(L):
+            kda.kda_commit(layers[l], cu, pools[l], si, recs[l][cur], nacc[s % S], record_rows=rr,
+                           pending=pending, eager=eag[s % S], stream=stream)
+
+    def timed(fn, K, with_events=False):
+        W = args.warmup
+        for s in range(W):
+            fn(s)
+        torch.cuda.synchronize()
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+               for _ in range(K)] if with_events else [None] * K
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(K):
+            fn(W + i, evs[i])   # step numbers continue, so the record buffers alternate
+        b.record(stream)
+        torch.cuda.synchronize()
+        kt = None
+        if with_events:
+            kt = float(np.mean([e[0].elapsed_time(e[1]) for step in evs for e in step]))
+        return a.elapsed_time(b) / K, kt
+
+    K = max(4, min(args.steps, 40))
+    ms_e, _ = timed(eager_step, K)
+    pending.zero_()
+    ms_d, kt_vd = timed(deferred_step, K, with_events=True)
+
+    valid = run.state_indices > 0
+    Tv = np.full(B, T)
+    be, bvd, bcd = [], [], []
+    for s in range(S):
+        n_prev = np.minimum(np.maximum(run.num_accepted((s - 1) % S), 0), Q)
+        n_now = np.minimum(np.maximum(run.num_accepted(s), 0), Q)
+        e_, v_, c_ = deferred_bytes(Tv, n_prev, run.eager((s - 1) % S), n_now, run.eager(s), valid, H)
+        be.append(e_); bvd.append(v_); bcd.append(c_)
+    b_eager, b_vdef, b_cdef = float(np.mean(be)), float(np.mean(bvd)), float(np.mean(bcd))
+    per_layer_e, per_layer_d = ms_e / L, ms_d / L
+    gbs_vd = b_vdef / (kt_vd * 1e6)
+    return {
+        "metric": "KDA verify+commit tokens/s and achieved HBM GB/s vs peak (B=64,H=32,T=4)",
+        "value": B * T * L / (ms_d * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_d,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"deferred: B={B} H={H} K=V=128 T={T} Q={Q}, {L} layers (own 1 GiB pool and "
+                        f"records each); a step = every layer's verify, then every layer's commit",
+            "B": B, "H": H, "K": 128, "V": 128, "T": T, "window": Q, "layers": L,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kda_verify_deferred",
+            "achieved": gbs_vd,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": gbs_vd / PEAK_HBM_GBS,
+            "traffic": measured_traffic("kda_verify_deferred"),
+        },
+        "flows": {
+            "eager": {"ms_per_layer_step": per_layer_e, "bytes_per_layer_step": b_eager,
+                      "gbs": b_eager / (per_layer_e * 1e6)},
+            "deferred": {"ms_per_layer_step": per_layer_d,
+                         "bytes_per_layer_step": b_vdef + b_cdef,
+                         "gbs": (b_vdef + b_cdef) / (per_layer_d * 1e6),
+                         "kda_verify_deferred_avg_us": kt_vd * 1e3},
+        },
+        "deferred_speedup": per_layer_e / per_layer_d,
+    }
 
 
 def cpu_baseline(batch, rows, seconds):
