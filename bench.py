@@ -141,6 +141,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU sample until this much wall time is spent")
+    ap.add_argument("--per-layer-commit", action="store_true",
+                    help="deferred workload: one kda_commit per layer instead of kda_commit_layers")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     return ap.parse_args()
@@ -446,13 +448,20 @@ def deferred_leg(args, torch, kda, dev):
     eag = [up(run.eager(s)) for s in range(S)]
     stream = torch.cuda.current_stream()
 
+    rec0 = [recs[l][0] for l in range(L)]
+    rec_by_parity = [[recs[l][c] for l in range(L)] for c in range(2)]
+
     def eager_step(s, ev=None):
         for l in range(L):
             kda.kda_verify(layers[l], *toks[l][:5], cu, pools[l], si, recs[l][0], o,
                            record_rows=rr, stream=stream)
-        for l in range(L):
-            kda.kda_commit(layers[l], cu, pools[l], si, recs[l][0], nacc[s % S], record_rows=rr,
-                           stream=stream)
+        if args.per_layer_commit:
+            for l in range(L):
+                kda.kda_commit(layers[l], cu, pools[l], si, recs[l][0], nacc[s % S],
+                               record_rows=rr, stream=stream)
+        else:   # every layer's commit in one launch
+            kda.kda_commit_layers(layers, cu, pools, si, rec0, nacc[s % S], record_rows=rr,
+                                  stream=stream)
 
     def deferred_step(s, ev=None):
         cur = s % 2
@@ -463,9 +472,13 @@ def deferred_leg(args, torch, kda, dev):
                                     pending, recs[l][cur], o, record_rows=rr, stream=stream)
             if ev is not None:
                 ev[l][1].record(stream)
-        for l in range(L):
-            kda.kda_commit(layers[l], cu, pools[l], si, recs[l][cur], nacc[s % S], record_rows=rr,
-                           pending=pending, eager=eag[s % S], stream=stream)
+        if args.per_layer_commit:
+            for l in range(L):
+                kda.kda_commit(layers[l], cu, pools[l], si, recs[l][cur], nacc[s % S],
+                               record_rows=rr, pending=pending, eager=eag[s % S], stream=stream)
+        else:
+            kda.kda_commit_layers(layers, cu, pools, si, rec_by_parity[cur], nacc[s % S],
+                                  record_rows=rr, pending=pending, eager=eag[s % S], stream=stream)
 
     def timed(fn, K, with_events=False):
         W = args.warmup
@@ -516,7 +529,8 @@ def deferred_leg(args, torch, kda, dev):
         "data": "synthetic",
         "config": {
             "workload": f"deferred: B={B} H={H} K=V=128 T={T} Q={Q}, {L} layers (own 1 GiB pool and "
-                        f"records each); a step = every layer's verify, then every layer's commit",
+                        f"records each); a step = every layer's verify, then every layer's commit "
+                        f"({'one launch per layer' if args.per_layer_commit else 'one launch for all layers'})",
             "B": B, "H": H, "K": 128, "V": 128, "T": T, "window": Q, "layers": L,
         },
         "roofline": {

@@ -190,6 +190,51 @@ kda_status kda_verify_deferred(const kda_layer* layer, const kda_tokens* tokens,
                                const int32_t* pending, const kda_records* rec_next,
                                const int32_t* record_rows, uint16_t* o, hipStream_t stream);
 
+/*
+ * kda_commit_layers -- kda_commit for several layers in one launch (pages:
+ * recoverssm.py, Glm5NextRecoverSSMCommitContext construction, which keeps
+ * per-layer base-address arrays, and its commit, whose kernels run over
+ * every layer in one grid; recoverssm.context, the deferred context's state
+ * commit over num_layers x num_heads). After acceptance every layer's commit
+ * is independent of the others, so one grid of layers x rows x heads x tiles
+ * replaces num_layers launches.
+ *   layers, pools, recs: HOST arrays of num_layers structs, 1..16 layers.
+ *   Every layer: the same num_heads and head_dim, records with the same rows
+ *   and window, and pools sharing one state_indices array (the same pointer:
+ *   a request's slot number is the same in every layer's pool).
+ *   cu_seqlens, num_rows, record_rows, num_accepted, pending, eager: shared,
+ *   with the meaning of kda_commit; each layer does exactly what kda_commit
+ *   would do for it (same bits). pending (deferred mode) holds one count per
+ *   record row for all layers and is written once.
+ * Errors as kda_commit, plus: num_layers outside 1..16, layers that differ
+ * in num_heads or record shape, or pools with different state_indices ->
+ * KDA_ERR_SHAPE; a layer's pool or records overlapping another layer's pool
+ * or records -> KDA_ERR_ALIAS.
+ */
+kda_status kda_commit_layers(const kda_layer* layers, const kda_pool* pools,
+                             const kda_records* recs, int32_t num_layers,
+                             const int32_t* cu_seqlens, int32_t num_rows,
+                             const int32_t* record_rows, const int32_t* num_accepted,
+                             int32_t* pending, const uint8_t* eager, hipStream_t stream);
+
+/*
+ * kda_flush_layers -- the flush of the deferred commit for several layers in
+ * one launch (pages: recoverssm.context, KDADeferredCommitContext.flush,
+ * which replays every pending commit without a verify). For each layer and
+ * each row with a slot in (0, num_slots): r = record_rows[i] (NULL: r = i),
+ * p = min(max(pending[r], 0), rec_prev->window) when 0 <= r < rows, else 0;
+ * replay records 0..p-1 of that layer's rec_prev row r from the slot and,
+ * if p > 0, store the state in place. This is kda_verify_deferred with every
+ * window empty, bit for bit; no token array is read and pending is read only.
+ *   layers, pools, rec_prev: HOST arrays of num_layers structs, 1..16 layers,
+ *   with the constraints of kda_commit_layers.
+ * Errors as kda_commit_layers; pending NULL -> KDA_ERR_NULL.
+ */
+kda_status kda_flush_layers(const kda_layer* layers, const kda_pool* pools,
+                            const kda_records* rec_prev, int32_t num_layers, int32_t num_rows,
+                            const int32_t* record_rows, const int32_t* pending,
+                            hipStream_t stream);
+
 /* Host: a static, human-readable name for a status code. */
 const char* kda_status_string(kda_status status);
 

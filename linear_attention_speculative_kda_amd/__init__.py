@@ -11,8 +11,11 @@ from .kda import (  # noqa: F401
     Layer,
     Records,
     allocate_records,
+    MAX_LAYERS,
     kda_commit,
+    kda_commit_layers,
     kda_flush,
+    kda_flush_layers,
     kda_recurrent,
     kda_verify,
     kda_verify_deferred,

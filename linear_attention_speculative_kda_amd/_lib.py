@@ -91,7 +91,12 @@ def load() -> ctypes.CDLL:
                                c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
     lib.kda_verify_deferred.argtypes = [P(KdaLayer), P(KdaTokens), P(KdaPool), P(KdaRecords),
                                         c_ptr, P(KdaRecords), c_ptr, c_ptr, c_ptr]
-    for fn in ("kda_recurrent", "kda_verify", "kda_commit", "kda_verify_deferred"):
+    lib.kda_commit_layers.argtypes = [P(KdaLayer), P(KdaPool), P(KdaRecords), ctypes.c_int32,
+                                      c_ptr, ctypes.c_int32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
+    lib.kda_flush_layers.argtypes = [P(KdaLayer), P(KdaPool), P(KdaRecords), ctypes.c_int32,
+                                     ctypes.c_int32, c_ptr, c_ptr, c_ptr]
+    for fn in ("kda_recurrent", "kda_verify", "kda_commit", "kda_verify_deferred",
+               "kda_commit_layers", "kda_flush_layers"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p

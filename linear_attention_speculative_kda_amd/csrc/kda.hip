@@ -93,7 +93,29 @@ struct Params {
   const int* pending_in;   // verify_deferred: read
   uint16_t* o;
   int tiles;               // V tiles per (row, head)
-  int total_blocks;
+  int total_blocks;        // workgroups of the launch (all layers)
+  int layer_blocks;        // workgroups per layer
+  int flush;               // deferred fold only: every window is empty, no token is read
+  int pending_skip;        // commit, deferred mode: this launch does not write pending
+};
+
+// Per-layer pointers of a multi-layer launch (the rest of Params is shared:
+// row metadata, state indices, head count, record window).
+constexpr int kMaxLayers = 16;
+struct LayerRef {
+  const float* a_log;
+  const float* g_bias;
+  float scale;
+  float lower_bound;
+  int has_lb;
+  int num_slots;
+  long long slot_stride;
+  float* state;
+  uint16_t *rk, *rv, *rg, *rb;                // commit: the records replayed
+  const uint16_t *pk, *pv, *pg, *pb;          // fold: the previous records
+};
+struct LayerTable {
+  LayerRef l[kMaxLayers];
 };
 
 // ---------------------------------------------------------------- helpers --
@@ -598,8 +620,9 @@ __device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, N
 
 // ------------------------------------------------------------------ kernel --
 
+// One workgroup's work: (row, head, tile) from its logical block index b.
 template <int MODE, int R, int TMAX>
-__global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
+__device__ __forceinline__ void kda_block(const Params& p, int b) {
   constexpr int BV = R * NWAVES * 8;   // value rows per workgroup
   constexpr bool kChunk = (MODE == kVerify || MODE == kDeferred);
   using StageT = typename std::conditional<kChunk, StageChunk<BV, CH>, Stage<BV, CH>>::type;
@@ -613,12 +636,6 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
   c.hw = c.tid >> 5;          // half-wave: token slot when staging
   c.l32 = c.tid & 31;         // 4 channels per lane when staging
 
-  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
-  // consecutive logical blocks (the V-tiles and heads of one request) are
-  // mapped to one XCD and share its L2.
-  int b = blockIdx.x;
-  const int nb = p.total_blocks;
-  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
   c.tile = b % p.tiles;
   const int rh = b / p.tiles;
   c.head = rh % p.H;
@@ -626,8 +643,9 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
   c.H = p.H;
 
   // ---- row prologue: span, slot, record row, counts -----------------------
-  const int bos = p.cu[row];
-  const int eos = p.cu[row + 1];
+  const bool flush = MODE == kDeferred && p.flush;
+  const int bos = flush ? 0 : p.cu[row];
+  const int eos = flush ? 0 : p.cu[row + 1];
   int T = eos - bos;
   if (bos < 0 || T < 0 || (MODE != kCommit && eos > p.num_tokens)) T = 0;
   c.bos = bos;
@@ -647,7 +665,7 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
     bool now = true;
     if (p.pending) {
       now = p.eager != nullptr && p.eager[row] != 0;
-      if (c.ri > 0 && c.head == 0 && c.tile == 0 && c.tid == 0)
+      if (!p.pending_skip && c.ri > 0 && c.head == 0 && c.tile == 0 && c.tid == 0)
         p.pending[c.ri - 1] = now ? 0 : (valid ? n : 0);
     }
     nfold = (valid && now) ? n : 0;
@@ -735,6 +753,45 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
     }
     if (MODE == kRecurrent) store_tile<R, BV>(S, sbase, c);
   }
+}
+
+// XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+// consecutive logical blocks (the V-tiles and heads of one request, the
+// layers of a multi-layer launch) are mapped to one XCD and share its L2.
+__device__ __forceinline__ int logical_block(int nb) {
+  const int b = blockIdx.x;
+  return (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+}
+
+template <int MODE, int R, int TMAX>
+__global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
+  kda_block<MODE, R, TMAX>(p, logical_block(p.total_blocks));
+}
+
+// The same work for several layers in one grid: logical block b belongs to
+// layer b / layer_blocks, whose pool, records and gate parameters replace
+// the shared ones.
+template <int MODE, int R, int TMAX>
+__global__ __launch_bounds__(NTHREADS) void kda_kernel_layers(Params p, LayerTable t) {
+  int b = logical_block(p.total_blocks);
+  const int l = b / p.layer_blocks;
+  b -= l * p.layer_blocks;
+  const LayerRef& L = t.l[l];
+  p.a_log = L.a_log;
+  p.g_bias = L.g_bias;
+  p.scale = L.scale;
+  p.lower_bound = L.lower_bound;
+  p.has_lb = L.has_lb;
+  p.num_slots = L.num_slots;
+  p.slot_stride = L.slot_stride;
+  p.state = L.state;
+  p.rk = L.rk; p.rv = L.rv; p.rg = L.rg; p.rb = L.rb;
+  p.pk = L.pk; p.pv = L.pv; p.pg = L.pg; p.pb = L.pb;
+  // pending is one array per request row, shared by the layers (they share
+  // the state indices, so every layer would write the same counts): layer 0
+  // writes it
+  if (l != 0) p.pending_skip = 1;
+  kda_block<MODE, R, TMAX>(p, b);
 }
 
 // ------------------------------------------------------------------- host --
@@ -923,6 +980,32 @@ kda_status launch_t(Params& p, hipStream_t stream) {
   }
 }
 
+template <int MODE, int R, int TMAX>
+kda_status launch_layers_r(Params& p, LayerTable& t, int num_layers, hipStream_t stream) {
+  p.tiles = KD / (32 * R);
+  const long long per = (long long)p.num_rows * p.H * p.tiles;
+  const long long blocks = per * num_layers;
+  if (blocks > 0x7FFFFFFFLL) return KDA_ERR_SHAPE;
+  p.layer_blocks = (int)per;
+  p.total_blocks = (int)blocks;
+  void* args[] = {&p, &t};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel_layers<MODE, R, TMAX>),
+                                       dim3((unsigned)blocks), dim3(NTHREADS), args, 0, stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+// Multi-layer launches: commit (per-token replay, any window) and the
+// deferred fold with empty windows (the flush).
+template <int MODE>
+kda_status launch_layers(Params& p, LayerTable& t, int num_layers, hipStream_t stream) {
+  constexpr int TMAX = MODE == kDeferred ? 4 : CH;   // the fold does not use the chunk path
+  switch (tile_rows_for(MODE, (long long)p.num_rows * p.H)) {
+    case 32: return launch_layers_r<MODE, 1, TMAX>(p, t, num_layers, stream);
+    case 64: return launch_layers_r<MODE, 2, TMAX>(p, t, num_layers, stream);
+    default: return launch_layers_r<MODE, 4, TMAX>(p, t, num_layers, stream);
+  }
+}
+
 template <int MODE>
 kda_status launch(Params& p, hipStream_t stream) {
   if ((MODE == kVerify || MODE == kDeferred) && p.Q <= 4) return launch_t<MODE, 4>(p, stream);
@@ -932,6 +1015,66 @@ kda_status launch(Params& p, hipStream_t stream) {
 }  // namespace
 
 // --------------------------------------------------------------- C ABI ----
+
+// Checks shared by the multi-layer calls: every layer valid, the same head
+// count, the same record shape, one state-index array, and no two layers'
+// pools or records overlapping each other or (with `pending`) the counts.
+kda_status check_layers(const kda_layer* layers, const kda_pool* pools, const kda_records* recs,
+                        int num_layers, int num_rows, const int32_t* pending) {
+  if (!layers || !pools || !recs) return KDA_ERR_NULL;
+  if (num_layers < 1 || num_layers > kMaxLayers || num_rows < 0) return KDA_ERR_SHAPE;
+  kda_status s;
+  const int H = layers[0].num_heads;
+  for (int l = 0; l < num_layers; ++l) {
+    if ((s = check_layer(&layers[l])) != KDA_OK) return s;
+    if (layers[l].num_heads != H) return KDA_ERR_SHAPE;
+    if ((s = check_pool(&pools[l], H, num_rows)) != KDA_OK) return s;
+    if ((s = check_records(&recs[l])) != KDA_OK) return s;
+    if (recs[l].rows != recs[0].rows || recs[l].window != recs[0].window) return KDA_ERR_SHAPE;
+    if (pools[l].state_indices != pools[0].state_indices) return KDA_ERR_SHAPE;
+  }
+  for (int l = 0; l < num_layers; ++l) {
+    const Range pl = pool_range(&pools[l], H);
+    Ranges rl;
+    record_ranges(&recs[l], H, rl);
+    if (records_self_overlap(rl)) return KDA_ERR_ALIAS;
+    for (int m = 0; m < num_layers; ++m) {
+      Ranges rm;
+      record_ranges(&recs[m], H, rm);
+      if (any_overlap(pl, rm)) return KDA_ERR_ALIAS;
+      if (m > l && overlap(pl, pool_range(&pools[m], H))) return KDA_ERR_ALIAS;
+      if (m > l)
+        for (int i = 0; i < rl.n; ++i)
+          if (any_overlap(rl.a[i], rm)) return KDA_ERR_ALIAS;
+    }
+    if (pending) {
+      const Range pr = range_of(pending, (long long)recs[0].rows * 4);
+      if (overlap(pr, pl) || any_overlap(pr, rl)) return KDA_ERR_ALIAS;
+    }
+  }
+  return KDA_OK;
+}
+
+void fill_layer_table(LayerTable& t, const kda_layer* layers, const kda_pool* pools,
+                      const kda_records* recs, int num_layers, bool fold) {
+  for (int l = 0; l < num_layers; ++l) {
+    LayerRef& r = t.l[l];
+    r.a_log = layers[l].a_log;
+    r.g_bias = layers[l].g_bias;
+    r.scale = layers[l].scale;
+    r.lower_bound = layers[l].lower_bound;
+    r.has_lb = layers[l].has_lower_bound ? 1 : 0;
+    r.num_slots = pools[l].num_slots;
+    r.slot_stride = pools[l].slot_stride;
+    r.state = pools[l].state;
+    r.rk = recs[l].k; r.rv = recs[l].v; r.rg = recs[l].g; r.rb = recs[l].beta;
+    if (fold) {
+      r.pk = recs[l].k; r.pv = recs[l].v; r.pg = recs[l].g; r.pb = recs[l].beta;
+    } else {
+      r.pk = r.pv = r.pg = r.pb = nullptr;
+    }
+  }
+}
 
 extern "C" {
 
@@ -1066,6 +1209,54 @@ kda_status kda_verify_deferred(const kda_layer* layer, const kda_tokens* tokens,
   p.pending_in = pending;
   p.o = o;
   return launch<kDeferred>(p, stream);
+}
+
+kda_status kda_commit_layers(const kda_layer* layers, const kda_pool* pools,
+                             const kda_records* recs, int32_t num_layers, const int32_t* cu_seqlens,
+                             int32_t num_rows, const int32_t* record_rows,
+                             const int32_t* num_accepted, int32_t* pending, const uint8_t* eager,
+                             hipStream_t stream) {
+  kda_status s = check_layers(layers, pools, recs, num_layers, num_rows, pending);
+  if (s != KDA_OK) return s;
+  if (!cu_seqlens || (num_rows > 0 && !num_accepted)) return KDA_ERR_NULL;
+  if (eager && !pending) return KDA_ERR_SHAPE;
+  if (num_rows == 0) return KDA_OK;
+  if (!record_rows && num_rows > recs[0].rows) return KDA_ERR_CAPACITY;
+  Params p = base_params(&layers[0]);
+  p.cu = cu_seqlens;
+  p.num_rows = num_rows;
+  p.num_tokens = 0x7FFFFFFF;
+  set_pool(p, &pools[0]);
+  set_records(p, &recs[0]);
+  p.record_rows = record_rows;
+  p.num_accepted = num_accepted;
+  p.pending = pending;
+  p.eager = eager;
+  LayerTable t{};
+  fill_layer_table(t, layers, pools, recs, num_layers, false);
+  return launch_layers<kCommit>(p, t, num_layers, stream);
+}
+
+kda_status kda_flush_layers(const kda_layer* layers, const kda_pool* pools,
+                            const kda_records* rec_prev, int32_t num_layers, int32_t num_rows,
+                            const int32_t* record_rows, const int32_t* pending, hipStream_t stream) {
+  kda_status s = check_layers(layers, pools, rec_prev, num_layers, num_rows, pending);
+  if (s != KDA_OK) return s;
+  if (!pending) return KDA_ERR_NULL;
+  if (num_rows == 0) return KDA_OK;
+  if (!record_rows && num_rows > rec_prev[0].rows) return KDA_ERR_CAPACITY;
+  Params p = base_params(&layers[0]);
+  p.num_rows = num_rows;
+  p.num_tokens = 0;
+  p.flush = 1;
+  set_pool(p, &pools[0]);
+  set_records(p, &rec_prev[0]);
+  p.pk = rec_prev[0].k; p.pv = rec_prev[0].v; p.pg = rec_prev[0].g; p.pb = rec_prev[0].beta;
+  p.record_rows = record_rows;
+  p.pending_in = pending;
+  LayerTable t{};
+  fill_layer_table(t, layers, pools, rec_prev, num_layers, true);
+  return launch_layers<kDeferred>(p, t, num_layers, stream);
 }
 
 const char* kda_status_string(kda_status status) {

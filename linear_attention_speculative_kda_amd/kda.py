@@ -239,3 +239,49 @@ def kda_flush(layer: Layer, pool, state_indices, rec_prev: Records, pending, rec
     kda_verify_deferred(layer, empty, empty, empty, empty,
                         torch.empty((0, H), dtype=torch.bfloat16, device=dev), cu, pool,
                         state_indices, rec_prev, pending, rec_next, empty, record_rows, stream)
+
+
+MAX_LAYERS = 16   # layers per multi-layer launch
+
+
+def _layer_arrays(layers, pools, state_indices, recs, rows: int):
+    n = len(layers)
+    if not (1 <= n <= MAX_LAYERS) or len(pools) != n or len(recs) != n:
+        raise ValueError(f"1..{MAX_LAYERS} layers with one pool and one record set each")
+    H = layers[0].num_heads
+    Ls = (_lib.KdaLayer * n)(*[l.c_struct() for l in layers])
+    Ps = (_lib.KdaPool * n)(*[_pool(p, state_indices, H, rows) for p in pools])
+    Rs = (_lib.KdaRecords * n)(*[r.c_struct() for r in recs])
+    return n, Ls, Ps, Rs
+
+
+def kda_commit_layers(layers, cu_seqlens, pools, state_indices, recs, num_accepted,
+                      record_rows=None, pending=None, eager=None, stream=None) -> None:
+    """kda_commit for every layer in one launch. The layers share the row
+    metadata and the state indices; each has its own pool and records."""
+    _on_gpu(pools[0], cu_seqlens, state_indices, num_accepted, record_rows, pending, eager,
+            *layers, *pools, *recs)
+    lib = _lib.load()
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    rows = cu_seqlens.numel() - 1
+    n, Ls, Ps, Rs = _layer_arrays(layers, pools, state_indices, recs, rows)
+    st = lib.kda_commit_layers(Ls, Ps, Rs, n, cu_seqlens.data_ptr(), rows,
+                               _opt_ptr(record_rows, torch.int32, "record_rows", rows),
+                               _opt_ptr(num_accepted, torch.int32, "num_accepted", rows),
+                               _opt_ptr(pending, torch.int32, "pending", recs[0].rows),
+                               _opt_ptr(eager, torch.uint8, "eager", rows), _stream(stream))
+    _lib.check("kda_commit_layers", st)
+
+
+def kda_flush_layers(layers, pools, state_indices, rec_prev, pending, record_rows=None,
+                     stream=None) -> None:
+    """Replay every pending commit of every layer in one launch (the flush)."""
+    _on_gpu(pools[0], state_indices, pending, record_rows, *layers, *pools, *rec_prev)
+    lib = _lib.load()
+    rows = state_indices.numel()
+    n, Ls, Ps, Rs = _layer_arrays(layers, pools, state_indices, rec_prev, rows)
+    st = lib.kda_flush_layers(Ls, Ps, Rs, n, rows,
+                              _opt_ptr(record_rows, torch.int32, "record_rows", rows),
+                              _opt_ptr(pending, torch.int32, "pending", rec_prev[0].rows),
+                              _stream(stream))
+    _lib.check("kda_flush_layers", st)

@@ -183,3 +183,65 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+# ------------------------------------------------------------ multi-layer --
+
+def layer_arrays(n=3, over=None):
+    """n layers, each with its own pool and records, far apart; `over` maps a
+    layer index to field overrides: {"layer": {...}, "pool": {...}, "rec": {...}}."""
+    over = over or {}
+    Ls, Ps, Rs = [], [], []
+    for l in range(n):
+        o = over.get(l, {})
+        Ls.append(layer(**o.get("layer", {})))
+        Ps.append(pool(**dict(dict(state=A + 0x10000000 * (l + 1)), **o.get("pool", {}))))
+        Rs.append(records(**dict(dict(base=A + 0x10000000 * (l + 1) + 0x8000000), **o.get("rec", {}))))
+    return ((_lib.KdaLayer * n)(*Ls), (_lib.KdaPool * n)(*Ps), (_lib.KdaRecords * n)(*Rs), n)
+
+
+def commit_layers(arrs=None, n_rows=2, pending=None, eager=None, acc=A + 0x600000, cu=A):
+    Ls, Ps, Rs, n = arrs or layer_arrays()
+    return _lib.load().kda_commit_layers(Ls, Ps, Rs, n, cu, n_rows, None, acc, pending, eager, None)
+
+
+def flush_layers(arrs=None, n_rows=2, pending=A + 0x700000):
+    Ls, Ps, Rs, n = arrs or layer_arrays()
+    return _lib.load().kda_flush_layers(Ls, Ps, Rs, n, n_rows, None, pending, None)
+
+
+def test_commit_layers_validation():
+    lib = _lib.load()
+    Ls, Ps, Rs, n = layer_arrays()
+    assert lib.kda_commit_layers(None, Ps, Rs, n, A, 2, None, A, None, None, None) == E["KDA_ERR_NULL"]
+    assert commit_layers(layer_arrays(1), cu=0) == E["KDA_ERR_NULL"]
+    assert commit_layers(layer_arrays(1), acc=0) == E["KDA_ERR_NULL"]
+    assert lib.kda_commit_layers(Ls, Ps, Rs, 0, A, 2, None, A, None, None, None) == E["KDA_ERR_SHAPE"]
+    assert commit_layers(layer_arrays(17)) == E["KDA_ERR_SHAPE"]
+    assert commit_layers(layer_arrays(3, {1: {"layer": dict(num_heads=H + 1)}})) == E["KDA_ERR_SHAPE"]
+    assert commit_layers(layer_arrays(3, {2: {"rec": dict(window=8)}})) == E["KDA_ERR_SHAPE"]
+    assert commit_layers(layer_arrays(3, {1: {"pool": dict(state_indices=A + 0x500100)}})) == E["KDA_ERR_SHAPE"]
+    assert commit_layers(layer_arrays(2, {1: {"layer": dict(head_dim=64)}})) == E["KDA_ERR_UNSUPPORTED"]
+    assert commit_layers(eager=A + 0x700000) == E["KDA_ERR_SHAPE"]       # eager without pending
+    assert commit_layers(n_rows=5) == E["KDA_ERR_CAPACITY"]
+    assert commit_layers(n_rows=0) == E["KDA_OK"]                         # no rows: no launch
+
+
+def test_commit_layers_aliasing():
+    # two layers sharing one pool
+    assert commit_layers(layer_arrays(2, {1: {"pool": dict(state=A + 0x10000000)}})) == E["KDA_ERR_ALIAS"]
+    # a layer's records inside another layer's pool
+    assert commit_layers(layer_arrays(2, {1: {"rec": dict(base=A + 0x10000000 + 0x1000)}})) == E["KDA_ERR_ALIAS"]
+    # two layers' records overlapping
+    assert commit_layers(layer_arrays(2, {1: {"rec": dict(base=A + 0x10000000 + 0x8000000 + 64)}})) == E["KDA_ERR_ALIAS"]
+    # pending inside a pool
+    assert commit_layers(pending=A + 0x20000000) == E["KDA_ERR_ALIAS"]
+
+
+def test_flush_layers_validation():
+    assert flush_layers(pending=0) == E["KDA_ERR_NULL"]
+    assert flush_layers(layer_arrays(17)) == E["KDA_ERR_SHAPE"]
+    assert flush_layers(layer_arrays(3, {1: {"rec": dict(rows=3)}})) == E["KDA_ERR_SHAPE"]
+    assert flush_layers(pending=A + 0x30000000) == E["KDA_ERR_ALIAS"]    # pending inside a pool
+    assert flush_layers(n_rows=5) == E["KDA_ERR_CAPACITY"]
+    assert flush_layers(n_rows=0) == E["KDA_OK"]
