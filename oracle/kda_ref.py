@@ -26,6 +26,11 @@ What it computes (sources are the four web pages on the method):
   checkpoint, writes outputs and raw records and leaves the checkpoint alone;
   commit replays the first n' = min(max(n, 0), T_i, Q) records and writes the
   checkpoint in place.
+* The commit plan and its align mode (recoverssm.py, ``_prepare_commit_plan_kernel``
+  and ``_replay_indices_kernel``): with a block table per request, the state
+  after the last committed token goes to the block holding that token and the
+  state at a crossed block boundary to that boundary's block; and the
+  conv-state compaction of the same commit (``_compact_conv_state_kernel``).
 * The deferred commit of the page "vllm.models.kimi_k3.nvidia.specialized_decode
   .recoverssm.context" (``KDADeferredCommitContext.commit`` / ``flush``,
   ``KDARecoverSSMDeferred``): commit turns n' into ``pending[record_row]``
@@ -249,11 +254,12 @@ def _store_state(pool: np.ndarray, slot: int, S: np.ndarray) -> None:
     pool[slot] = f64_to_f32(S.transpose(0, 2, 1))
 
 
-def _replay(layer: Layer, S: np.ndarray, rec: Records, ri: int, n: int) -> np.ndarray:
-    """Run the first n records of storage row ri through the recurrence
+def _replay(layer: Layer, S: np.ndarray, rec: Records, ri: int, n: int,
+            start: int = 0) -> np.ndarray:
+    """Run records start .. n-1 of storage row ri through the recurrence
     (no output: the commit only needs the state)."""
     H, K = S.shape[0], S.shape[1]
-    for t in range(n):
+    for t in range(start, n):
         _, k_hat, v, g, beta = _prepare(layer, H, K, None, rec.k[ri, :, t],
                                         rec.v[ri, :, t], rec.g[ri, :, t],
                                         rec.beta[ri, :, t])
@@ -340,6 +346,109 @@ def kda_commit(layer: Layer, cu_seqlens, num_tokens: int, pool, state_indices,
                 pending[ri - 1] = 0 if now else (n if valid else 0)
         if valid and now:
             _store_state(pool, slot, _replay(layer, _load_state(pool, slot), rec, ri, n))
+
+
+@dataclass
+class Align:
+    """Align mode of the commit: one row of block ids per request row (block 0
+    is the null block), the tokens each request had cached before the step,
+    and the tokens per block."""
+    block_table: np.ndarray    # int32 [rows, width]
+    num_computed: np.ndarray   # int32 [rows]
+    block_size: int
+
+
+def commit_plan(cu_seqlens, num_tokens: int, num_accepted, state_indices, Q: int,
+                align: Align | None = None) -> np.ndarray:
+    """Per row (n', final block, boundary block, boundary length), as
+    ``_prepare_commit_plan_kernel`` computes them (int64 [rows, 4]).
+
+    n' = min(max(n, 0), T_i, Q). Without align the final block is the source
+    (the row's state index) and there is no boundary. With align, c = tokens
+    cached before the step (a negative count counts as 0, a reading):
+      final column    = min(max(c + n' - 1, 0) // block_size, width - 1)
+      next boundary   = (c // block_size + 1) * block_size
+      boundary length = next boundary - c
+      boundary block  = the block at column next boundary // block_size - 1
+                        when c + n' reaches the next boundary (and that column
+                        is inside the table, a reading), else the null block.
+    Rows with a source <= 0 or n' = 0 get (0, 0, 0, 0)."""
+    N = len(state_indices)
+    plan = np.zeros((N, 4), np.int64)
+    for i in range(N):
+        _, T = _row_span(cu_seqlens, i, num_tokens)
+        n = commit_length(num_accepted[i], T, Q)
+        src = int(state_indices[i])
+        final, bnd, blen = src, 0, 0
+        if align is not None:
+            bs = int(align.block_size)
+            width = align.block_table.shape[1]
+            c = max(int(align.num_computed[i]), 0)
+            col = min(max(c + n - 1, 0) // bs, width - 1)
+            final = int(align.block_table[i, col])
+            nb = (c // bs + 1) * bs
+            blen = nb - c
+            bcol = nb // bs - 1
+            if c + n >= nb and bcol < width:
+                bnd = int(align.block_table[i, bcol])
+        if src > 0 and n > 0:
+            plan[i] = (n, final, bnd, blen)
+    return plan
+
+
+def kda_commit_align(layer: Layer, cu_seqlens, num_tokens: int, pool, state_indices,
+                     rec: Records, num_accepted, align: Align, record_rows=None) -> None:
+    """The commit in align mode (``_replay_indices_kernel`` and the commit's
+    replay): replay the first n' records from the source block; the state
+    after the first boundary-length records goes to the boundary block when
+    that length is below n' and the block is not null; the state after n'
+    records goes to the final block. A row is skipped without a source, a
+    final block (not null and inside the pool) or a record row. Blocks that
+    are out of the pool are not written (a reading for memory safety).
+    Destination blocks are assumed to be no other row's source."""
+    plan = commit_plan(cu_seqlens, num_tokens, num_accepted, state_indices, rec.window, align)
+    nslots = pool.shape[0]
+    for i in range(len(state_indices)):
+        n, final, bnd, blen = (int(x) for x in plan[i])
+        src = int(state_indices[i])
+        ri = _record_index(record_rows, i, rec.rows)
+        if n == 0 or ri == 0 or not _slot_ok(src, nslots) or not _slot_ok(final, nslots):
+            continue
+        S = _load_state(pool, src)
+        if 0 < blen < n and _slot_ok(bnd, nslots):
+            S = _replay(layer, S, rec, ri, blen)
+            _store_state(pool, bnd, S)
+            S = _replay(layer, S, rec, ri, n, start=blen)
+        else:
+            S = _replay(layer, S, rec, ri, n)
+        _store_state(pool, final, S)
+
+
+def conv_compact(conv: np.ndarray, cu_seqlens, num_tokens: int, num_accepted, state_indices,
+                 Q: int, history: int, align: Align | None = None) -> None:
+    """The conv-state compaction of the commit (``_compact_conv_state_kernel``).
+
+    conv [blocks, channels, width], any element type, copied exactly. After a
+    verify, the token axis of a row's source block holds the last history - 1
+    inputs before the window, then the window's inputs; after n' accepted
+    tokens the last ``history`` inputs are columns n' - 1 .. n' + history - 2.
+    They move to columns 0 .. history - 1 of the final block (the source
+    itself without align). In align mode the columns from boundary length - 1
+    also go to the boundary block, when there is one. Rows without a source
+    or final block inside the table, or with n' = 0, are left alone; all of a
+    row's reads come before its writes."""
+    plan = commit_plan(cu_seqlens, num_tokens, num_accepted, state_indices, Q, align)
+    nb = conv.shape[0]
+    for i in range(len(state_indices)):
+        n, final, bnd, blen = (int(x) for x in plan[i])
+        src = int(state_indices[i])
+        if n == 0 or not 0 < src < nb or not 0 < final < nb:
+            continue
+        vals = conv[src, :, n - 1:n - 1 + history].copy()
+        if align is not None and 0 < bnd < nb:
+            bvals = conv[src, :, blen - 1:blen - 1 + history].copy()
+            conv[bnd, :, :history] = bvals
+        conv[final, :, :history] = vals
 
 
 def kda_verify_deferred(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indices,

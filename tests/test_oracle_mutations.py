@@ -31,7 +31,22 @@ MUTATIONS = {
         '    o = None if q_hat is None else np.einsum("...kv,...k->...v", S, q_hat)\n    S = S + k_hat[..., :, None] * u[..., None, :]'),
     "no window clamp": ("return min(max(int(n), 0), int(T), int(Q))", "return min(max(int(n), 0), int(T))"),
     "beta missing from the delta": ("u = beta[..., None] * (v - ", "u = (v - "),
+    "final column one token late": ("col = min(max(c + n - 1, 0) // bs, width - 1)",
+                                    "col = min(max(c + n, 0) // bs, width - 1)"),
+    "final column not clamped": ("col = min(max(c + n - 1, 0) // bs, width - 1)",
+                                 "col = max(c + n - 1, 0) // bs"),
+    "boundary reached strictly": ("if c + n >= nb and bcol < width:", "if c + n > nb and bcol < width:"),
+    "boundary length off by one": ("blen = nb - c\n", "blen = nb - c - 1\n"),
+    "boundary column one block late": ("bcol = nb // bs - 1", "bcol = nb // bs"),
+    "align replay restarts at 0": ("S = _replay(layer, S, rec, ri, n, start=blen)",
+                                   "S = _replay(layer, S, rec, ri, n)"),
+    "conv window one column late": ("vals = conv[src, :, n - 1:n - 1 + history].copy()",
+                                    "vals = conv[src, :, n:n + history].copy()"),
+    "conv boundary takes the final window": ("bvals = conv[src, :, blen - 1:blen - 1 + history].copy()",
+                                             "bvals = conv[src, :, n - 1:n - 1 + history].copy()"),
 }
+
+PIN_FILES = ("test_oracle.py", "test_oracle_commit_align.py")
 
 
 def _run_pins(tmp_path, src):
@@ -45,11 +60,12 @@ def _run_pins(tmp_path, src):
                     ignore=shutil.ignore_patterns("__pycache__"))
     tdir = tmp_path / "pins"
     tdir.mkdir()
-    shutil.copy(os.path.join(ROOT, "tests", "test_oracle.py"), tdir / "test_oracle.py")
+    for f in PIN_FILES:
+        shutil.copy(os.path.join(ROOT, "tests", f), tdir / f)
     shutil.copytree(os.path.join(ROOT, "tests", "golden"), tdir / "golden")
     env = dict(os.environ, PYTHONPATH=str(tmp_path))
     res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                          "--rootdir", str(tmp_path), str(tdir / "test_oracle.py")],
+                          "--rootdir", str(tmp_path), *[str(tdir / f) for f in PIN_FILES]],
                          cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=300)
     assert "passed" in res.stdout or "failed" in res.stdout, res.stdout[-2000:] + res.stderr[-2000:]
     return res
