@@ -115,6 +115,35 @@ typedef struct kda_records {
   int32_t window;           /* Q: tokens per record row, 1..64 */
 } kda_records;
 
+/* Align mode of the commit (host struct of device pointers; pages:
+ * recoverssm.py, _prepare_commit_plan_kernel with its align mode and
+ * _replay_indices_kernel). Per request row i, with c = num_computed[i] (the
+ * tokens cached before the step; negative counts as 0) and bs = block_size:
+ *   final block    = block_table[i][min(max(c + n' - 1, 0) / bs, width - 1)]
+ *   next boundary  = (c / bs + 1) * bs, boundary length = next - c
+ *   boundary block = block_table[i][next / bs - 1] when c + n' >= next and that
+ *                    column is below width, else none.
+ * The state after n' records goes to the final block; the state after the
+ * boundary length goes to the boundary block when that length is below n'.
+ * Block 0 is the null block: a row whose final block is 0 (or outside the
+ * pool) commits nothing. Destination blocks must not be another row's
+ * source. */
+typedef struct kda_align {
+  const int32_t* block_table;   /* [num_rows, width] int32, row stride row_stride elements */
+  int64_t row_stride;           /* >= width */
+  int32_t width;                /* >= 1 */
+  const int32_t* num_computed;  /* [num_rows] int32 */
+  int32_t block_size;           /* tokens per block, >= 1 */
+} kda_align;
+
+/* One layer's conv state (host struct of a device pointer): 16-bit elements
+ * [num_blocks, channels, width] with element strides. */
+typedef struct kda_conv_state {
+  uint16_t* state;
+  int64_t block_stride, dim_stride, token_stride;   /* elements, >= 1 */
+  int32_t num_blocks;
+} kda_conv_state;
+
 /*
  * kda_recurrent -- the plain full-state recurrence (pages: recoverssm.py,
  * _verify_kernel's per-token body, which is the stock fused recurrent KDA
@@ -206,16 +235,22 @@ kda_status kda_verify_deferred(const kda_layer* layer, const kda_tokens* tokens,
  *   with the meaning of kda_commit; each layer does exactly what kda_commit
  *   would do for it (same bits). pending (deferred mode) holds one count per
  *   record row for all layers and is written once.
+ *   align (host struct, may be NULL): the align mode above, which writes
+ *   the final (and boundary) block instead of the source; only without
+ *   pending (deferred mode with align -> KDA_ERR_UNSUPPORTED).
  * Errors as kda_commit, plus: num_layers outside 1..16, layers that differ
  * in num_heads or record shape, or pools with different state_indices ->
  * KDA_ERR_SHAPE; a layer's pool or records overlapping another layer's pool
- * or records -> KDA_ERR_ALIAS.
+ * or records -> KDA_ERR_ALIAS; align with a NULL table or count array ->
+ * KDA_ERR_NULL, with width < 1, block_size < 1 or row_stride < width ->
+ * KDA_ERR_SHAPE.
  */
 kda_status kda_commit_layers(const kda_layer* layers, const kda_pool* pools,
                              const kda_records* recs, int32_t num_layers,
                              const int32_t* cu_seqlens, int32_t num_rows,
                              const int32_t* record_rows, const int32_t* num_accepted,
-                             int32_t* pending, const uint8_t* eager, hipStream_t stream);
+                             int32_t* pending, const uint8_t* eager, const kda_align* align,
+                             hipStream_t stream);
 
 /*
  * kda_flush_layers -- the flush of the deferred commit for several layers in
@@ -234,6 +269,34 @@ kda_status kda_flush_layers(const kda_layer* layers, const kda_pool* pools,
                             const kda_records* rec_prev, int32_t num_layers, int32_t num_rows,
                             const int32_t* record_rows, const int32_t* pending,
                             hipStream_t stream);
+
+/*
+ * kda_conv_compact -- the conv-state half of the commit, for num_layers
+ * layers in one launch (pages: recoverssm.py, _compact_conv_state_kernel).
+ * After a verify, the token axis of a row's conv-state block holds the last
+ * history - 1 inputs before the window, then the window's inputs. For each
+ * layer and row i with 0 < state_indices[i] < num_blocks and
+ * n' = min(max(num_accepted[i], 0), T_i, window) > 0: columns n' - 1 ..
+ * n' + history - 2 of the source block move to columns 0 .. history - 1 of
+ * the final block (the source itself when align is NULL; see kda_align);
+ * in align mode the columns from boundary length - 1 also go to the
+ * boundary block, when there is one. Every row reads before it writes;
+ * values are copied as 16-bit patterns. Blocks outside 1..num_blocks-1 are
+ * skipped.
+ *   layers: HOST array of num_layers (1..64) conv states.
+ *   conv_dim: channels (>= 1); history: 1..8; width: columns of the token
+ *   axis, >= window + history - 1; window: 1..64.
+ *   cu_seqlens [num_rows + 1], state_indices, num_accepted [num_rows] int32;
+ *   num_rows <= 65535.
+ * Errors: NULL pointers -> KDA_ERR_NULL; sizes out of range ->
+ * KDA_ERR_SHAPE; a misaligned state -> KDA_ERR_ALIGN; two layers' states
+ * overlapping -> KDA_ERR_ALIAS; align as for kda_commit_layers.
+ */
+kda_status kda_conv_compact(const kda_conv_state* layers, int32_t num_layers, int32_t conv_dim,
+                            int32_t history, int32_t width, const int32_t* cu_seqlens,
+                            int32_t num_rows, const int32_t* state_indices,
+                            const int32_t* num_accepted, int32_t window,
+                            const kda_align* align, hipStream_t stream);
 
 /* Host: a static, human-readable name for a status code. */
 const char* kda_status_string(kda_status status);

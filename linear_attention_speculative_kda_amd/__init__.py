@@ -8,12 +8,14 @@ not been built.
 
 from .kda import (  # noqa: F401
     HEAD_DIM,
+    Align,
     Layer,
     Records,
     allocate_records,
     MAX_LAYERS,
     kda_commit,
     kda_commit_layers,
+    kda_conv_compact,
     kda_flush,
     kda_flush_layers,
     kda_recurrent,

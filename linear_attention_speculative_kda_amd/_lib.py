@@ -64,6 +64,25 @@ class KdaRecords(ctypes.Structure):
     ]
 
 
+class KdaAlign(ctypes.Structure):
+    _fields_ = [
+        ("block_table", c_ptr),
+        ("row_stride", ctypes.c_int64),
+        ("width", ctypes.c_int32),
+        ("num_computed", c_ptr),
+        ("block_size", ctypes.c_int32),
+    ]
+
+
+class KdaConvState(ctypes.Structure):
+    _fields_ = [
+        ("state", c_ptr),
+        ("block_stride", ctypes.c_int64), ("dim_stride", ctypes.c_int64),
+        ("token_stride", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int32),
+    ]
+
+
 class KdaError(RuntimeError):
     def __init__(self, call: str, status: int, message: str):
         super().__init__(f"{call}: {message}")
@@ -92,11 +111,15 @@ def load() -> ctypes.CDLL:
     lib.kda_verify_deferred.argtypes = [P(KdaLayer), P(KdaTokens), P(KdaPool), P(KdaRecords),
                                         c_ptr, P(KdaRecords), c_ptr, c_ptr, c_ptr]
     lib.kda_commit_layers.argtypes = [P(KdaLayer), P(KdaPool), P(KdaRecords), ctypes.c_int32,
-                                      c_ptr, ctypes.c_int32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
+                                      c_ptr, ctypes.c_int32, c_ptr, c_ptr, c_ptr, c_ptr,
+                                      P(KdaAlign), c_ptr]
+    lib.kda_conv_compact.argtypes = [P(KdaConvState), ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, c_ptr, ctypes.c_int32, c_ptr,
+                                     c_ptr, ctypes.c_int32, P(KdaAlign), c_ptr]
     lib.kda_flush_layers.argtypes = [P(KdaLayer), P(KdaPool), P(KdaRecords), ctypes.c_int32,
                                      ctypes.c_int32, c_ptr, c_ptr, c_ptr]
     for fn in ("kda_recurrent", "kda_verify", "kda_commit", "kda_verify_deferred",
-               "kda_commit_layers", "kda_flush_layers"):
+               "kda_commit_layers", "kda_flush_layers", "kda_conv_compact"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p

@@ -51,6 +51,49 @@ constexpr int MAX_WINDOW = 64;
 
 enum Mode : int { kRecurrent = 0, kVerify = 1, kCommit = 2, kDeferred = 3 };
 
+// Align mode of the commit: a row of block ids per request row, the tokens
+// each request had cached before the step, and the tokens per block.
+struct AlignRef {
+  const int* bt;           // nullptr: no align mode
+  long long row_stride;    // elements between rows of bt
+  int width;
+  const int* num_computed;
+  int block_size;
+};
+
+// A row's commit plan (recoverssm.py, _prepare_commit_plan_kernel): n', the
+// final block (the source without align; in align mode the block holding the
+// last committed token), and the boundary block (0: none) and length. A
+// negative cached count counts as 0, and a boundary column beyond the block
+// table gives no boundary block.
+struct Plan {
+  int n, final_block, boundary_block, boundary_len;
+};
+
+__device__ __forceinline__ Plan commit_plan_row(const AlignRef& al, int row, int n, int src) {
+  Plan pl;
+  pl.n = n;
+  pl.final_block = src;
+  pl.boundary_block = 0;
+  pl.boundary_len = 0;
+  if (al.bt) {
+    const long long bs = al.block_size;
+    long long cached = al.num_computed[row];
+    cached = cached < 0 ? 0 : cached;
+    long long last = cached + n - 1;
+    last = last < 0 ? 0 : last;
+    long long col = last / bs;
+    col = col < al.width - 1 ? col : al.width - 1;
+    const int* bt_row = al.bt + (long long)row * al.row_stride;
+    pl.final_block = bt_row[col];
+    const long long next = (cached / bs + 1) * bs;
+    pl.boundary_len = (int)(next - cached);
+    const long long bcol = next / bs - 1;
+    if (cached + n >= next && bcol < al.width) pl.boundary_block = bt_row[bcol];
+  }
+  return pl;
+}
+
 struct Params {
   // layer
   const float* a_log;
@@ -97,6 +140,7 @@ struct Params {
   int layer_blocks;        // workgroups per layer
   int flush;               // deferred fold only: every window is empty, no token is read
   int pending_skip;        // commit, deferred mode: this launch does not write pending
+  AlignRef align;          // commit: block table (align.bt == nullptr: in place)
 };
 
 // Per-layer pointers of a multi-layer launch (the rest of Params is shared:
@@ -656,12 +700,26 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
 
   int nfold = 0;   // records replayed into the state (commit / deferred fold)
   int nmain = 0;   // window tokens run with outputs (recurrent / verify)
+  float* fbase = nullptr;   // commit: where the final state goes (the source without align)
+  float* bbase = nullptr;   // align mode: where the boundary state goes, after blen records
+  int blen = 0;
   if (MODE == kCommit) {
     int n = p.num_accepted[row];
     n = n < 0 ? 0 : n;
     n = n < T ? n : T;
     n = n < p.Q ? n : p.Q;
-    const bool valid = slot_ok && n > 0 && c.ri > 0;
+    bool final_ok = true;
+    if (p.align.bt && slot_ok && n > 0) {
+      const Plan pl = commit_plan_row(p.align, row, n, slot);
+      final_ok = pl.final_block > 0 && pl.final_block < p.num_slots;
+      const long long head_off = (long long)c.head * KD * KD;
+      if (final_ok) fbase = p.state + (long long)pl.final_block * p.slot_stride + head_off;
+      if (pl.boundary_len < n && pl.boundary_block > 0 && pl.boundary_block < p.num_slots) {
+        bbase = p.state + (long long)pl.boundary_block * p.slot_stride + head_off;
+        blen = pl.boundary_len;
+      }
+    }
+    const bool valid = slot_ok && n > 0 && c.ri > 0 && final_ok;
     bool now = true;
     if (p.pending) {
       now = p.eager != nullptr && p.eager[row] != 0;
@@ -682,6 +740,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   if (!slot_ok || (nfold == 0 && nmain == 0)) return;
   c.A = exp_hw(scalar_load(p.a_log + c.head));
   float* sbase = p.state + (long long)slot * p.slot_stride + (long long)c.head * KD * KD;
+  if (fbase == nullptr) fbase = sbase;
   const bool chunk = kChunk && nmain <= TMAX;
 
   // Verify of a window that fits one chunk: straight-line code from the
@@ -711,7 +770,9 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   // inputs only while the 64 KiB tile is still in flight.
   Raw<BV> raw;
   const bool first_fold = nfold > 0;
-  stage_load<MODE, BV>(raw, p, c, first_fold, 0, first_fold ? (nfold < CH ? nfold : CH)
+  // align mode: the replay stops at blen for the boundary store
+  const int seg0 = (bbase != nullptr) ? blen : nfold;
+  stage_load<MODE, BV>(raw, p, c, first_fold, 0, first_fold ? (seg0 < CH ? seg0 : CH)
                                                              : (nmain < CH ? nmain : CH));
   __builtin_amdgcn_sched_barrier(0);
   float S[R][16];
@@ -720,15 +781,18 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
 
   // ---- fold: replay records into the state (commit, deferred fold) --------
   if (nfold > 0) {
-    for (int c0 = 0; c0 < nfold; c0 += CH) {
-      const int m = (nfold - c0) < CH ? (nfold - c0) : CH;
+    for (int c0 = 0; c0 < nfold;) {
+      const int end = (bbase != nullptr && c0 < blen) ? blen : nfold;
+      const int m = (end - c0) < CH ? (end - c0) : CH;
       if (c0 > 0) stage_load<MODE, BV>(raw, p, c, true, c0, m);
       lds_barrier();  // the previous chunk is consumed
       stage_compute<MODE, BV, CH>(st, raw, p, c, true, c0);
       lds_barrier();
       seq_tokens<R, BV, CH>(S, st, p, c, m, false, 0);
+      c0 += m;
+      if (bbase != nullptr && c0 == blen) store_tile<R, BV>(S, bbase, c);
     }
-    store_tile<R, BV>(S, sbase, c);
+    store_tile<R, BV>(S, fbase, c);
     if (nmain > 0) stage_load<MODE, BV>(raw, p, c, false, 0, nmain < CH ? nmain : CH);
   }
 
@@ -792,6 +856,77 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel_layers(Params p, LayerTab
   // writes it
   if (l != 0) p.pending_skip = 1;
   kda_block<MODE, R, TMAX>(p, b);
+}
+
+// ------------------------------------------------------- conv compaction --
+//
+// The other half of the commit (recoverssm.py, _compact_conv_state_kernel):
+// after a verify, the token axis of a row's conv-state block holds the last
+// history - 1 inputs before the window and then the window's inputs; after n'
+// accepted tokens the last `history` inputs are columns n' - 1 ..
+// n' + history - 2, and they move to columns 0 .. history - 1 of the final
+// block (in align mode the columns from boundary_len - 1 also go to the
+// boundary block). One thread per (channel, row, layer); a thread reads all
+// of its values before it writes any. The element values are copied as 16-bit
+// patterns.
+constexpr int kMaxConvLayers = 64;
+constexpr int kMaxHistory = 8;
+constexpr int kConvThreads = 256;
+
+struct ConvRef {
+  uint16_t* state;
+  long long block_stride, dim_stride, token_stride;
+  int num_blocks;
+};
+struct ConvParams {
+  const int* cu;
+  const int* slots;
+  const int* num_accepted;
+  int num_rows, conv_dim, history, window;
+  AlignRef align;
+};
+struct ConvTable {
+  ConvRef l[kMaxConvLayers];
+};
+
+__global__ __launch_bounds__(kConvThreads) void conv_compact_kernel(ConvParams p, ConvTable t) {
+  const int d = blockIdx.x * kConvThreads + threadIdx.x;
+  const int row = blockIdx.y;
+  const ConvRef& L = t.l[blockIdx.z];
+  const int src = p.slots[row];
+  if (src <= 0 || src >= L.num_blocks) return;
+  const int bos = p.cu[row], eos = p.cu[row + 1];
+  int T = eos - bos;
+  if (bos < 0 || T < 0) T = 0;
+  int n = p.num_accepted[row];
+  n = n < 0 ? 0 : n;
+  n = n < T ? n : T;
+  n = n < p.window ? n : p.window;
+  if (n == 0) return;
+  const Plan pl = commit_plan_row(p.align, row, n, src);
+  if (pl.final_block <= 0 || pl.final_block >= L.num_blocks) return;
+  const bool boundary = p.align.bt != nullptr && pl.boundary_block > 0 &&
+                        pl.boundary_block < L.num_blocks;
+  if (d >= p.conv_dim) return;
+  const uint16_t* in = L.state + (long long)src * L.block_stride + (long long)d * L.dim_stride;
+  uint16_t fv[kMaxHistory], bv[kMaxHistory];
+#pragma unroll
+  for (int j = 0; j < kMaxHistory; ++j) {
+    if (j < p.history) {
+      fv[j] = in[(long long)(n - 1 + j) * L.token_stride];
+      if (boundary) bv[j] = in[(long long)(pl.boundary_len - 1 + j) * L.token_stride];
+    }
+  }
+  if (boundary) {
+    uint16_t* out = L.state + (long long)pl.boundary_block * L.block_stride + (long long)d * L.dim_stride;
+#pragma unroll
+    for (int j = 0; j < kMaxHistory; ++j)
+      if (j < p.history) out[(long long)j * L.token_stride] = bv[j];
+  }
+  uint16_t* out = L.state + (long long)pl.final_block * L.block_stride + (long long)d * L.dim_stride;
+#pragma unroll
+  for (int j = 0; j < kMaxHistory; ++j)
+    if (j < p.history) out[(long long)j * L.token_stride] = fv[j];
 }
 
 // ------------------------------------------------------------------- host --
@@ -1016,6 +1151,31 @@ kda_status launch(Params& p, hipStream_t stream) {
 
 // --------------------------------------------------------------- C ABI ----
 
+kda_status check_align(const kda_align* a, int num_rows) {
+  if (!a) return KDA_OK;
+  if (num_rows > 0 && (!a->block_table || !a->num_computed)) return KDA_ERR_NULL;
+  if (a->width < 1 || a->block_size < 1 || a->row_stride < a->width) return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+AlignRef align_ref(const kda_align* a) {
+  AlignRef r{};
+  if (a) {
+    r.bt = a->block_table;
+    r.row_stride = a->row_stride;
+    r.width = a->width;
+    r.num_computed = a->num_computed;
+    r.block_size = a->block_size;
+  }
+  return r;
+}
+
+// Elements spanned by one layer's conv state: the last element's offset + 1.
+long long conv_span(const kda_conv_state* c, int conv_dim, int width) {
+  return (long long)(c->num_blocks - 1) * c->block_stride + (long long)(conv_dim - 1) * c->dim_stride +
+         (long long)(width - 1) * c->token_stride + 1;
+}
+
 // Checks shared by the multi-layer calls: every layer valid, the same head
 // count, the same record shape, one state-index array, and no two layers'
 // pools or records overlapping each other or (with `pending`) the counts.
@@ -1215,11 +1375,13 @@ kda_status kda_commit_layers(const kda_layer* layers, const kda_pool* pools,
                              const kda_records* recs, int32_t num_layers, const int32_t* cu_seqlens,
                              int32_t num_rows, const int32_t* record_rows,
                              const int32_t* num_accepted, int32_t* pending, const uint8_t* eager,
-                             hipStream_t stream) {
+                             const kda_align* align, hipStream_t stream) {
   kda_status s = check_layers(layers, pools, recs, num_layers, num_rows, pending);
   if (s != KDA_OK) return s;
   if (!cu_seqlens || (num_rows > 0 && !num_accepted)) return KDA_ERR_NULL;
   if (eager && !pending) return KDA_ERR_SHAPE;
+  if ((s = check_align(align, num_rows)) != KDA_OK) return s;
+  if (align && pending) return KDA_ERR_UNSUPPORTED;
   if (num_rows == 0) return KDA_OK;
   if (!record_rows && num_rows > recs[0].rows) return KDA_ERR_CAPACITY;
   Params p = base_params(&layers[0]);
@@ -1232,6 +1394,7 @@ kda_status kda_commit_layers(const kda_layer* layers, const kda_pool* pools,
   p.num_accepted = num_accepted;
   p.pending = pending;
   p.eager = eager;
+  p.align = align_ref(align);
   LayerTable t{};
   fill_layer_table(t, layers, pools, recs, num_layers, false);
   return launch_layers<kCommit>(p, t, num_layers, stream);
@@ -1257,6 +1420,58 @@ kda_status kda_flush_layers(const kda_layer* layers, const kda_pool* pools,
   LayerTable t{};
   fill_layer_table(t, layers, pools, rec_prev, num_layers, true);
   return launch_layers<kDeferred>(p, t, num_layers, stream);
+}
+
+kda_status kda_conv_compact(const kda_conv_state* layers, int32_t num_layers, int32_t conv_dim,
+                            int32_t history, int32_t width, const int32_t* cu_seqlens,
+                            int32_t num_rows, const int32_t* state_indices,
+                            const int32_t* num_accepted, int32_t window, const kda_align* align,
+                            hipStream_t stream) {
+  if (!layers) return KDA_ERR_NULL;
+  if (num_layers < 1 || num_layers > kMaxConvLayers || num_rows < 0 || conv_dim < 1 ||
+      history < 1 || history > kMaxHistory || window < 1 || window > MAX_WINDOW ||
+      width < window + history - 1)
+    return KDA_ERR_SHAPE;
+  for (int l = 0; l < num_layers; ++l) {
+    const kda_conv_state& c = layers[l];
+    if (!c.state) return KDA_ERR_NULL;
+    if (c.num_blocks < 1 || c.block_stride < 1 || c.dim_stride < 1 || c.token_stride < 1)
+      return KDA_ERR_SHAPE;
+    if (!aligned(c.state, 2)) return KDA_ERR_ALIGN;
+  }
+  for (int l = 0; l < num_layers; ++l)
+    for (int m = l + 1; m < num_layers; ++m)
+      if (overlap(range_of(layers[l].state, conv_span(&layers[l], conv_dim, width) * 2),
+                  range_of(layers[m].state, conv_span(&layers[m], conv_dim, width) * 2)))
+        return KDA_ERR_ALIAS;
+  if (num_rows > 0 && (!cu_seqlens || !state_indices || !num_accepted)) return KDA_ERR_NULL;
+  kda_status s;
+  if ((s = check_align(align, num_rows)) != KDA_OK) return s;
+  if (num_rows == 0) return KDA_OK;
+  if (num_rows > 65535) return KDA_ERR_SHAPE;   // rows are the grid's second dimension
+  ConvParams p{};
+  p.cu = cu_seqlens;
+  p.slots = state_indices;
+  p.num_accepted = num_accepted;
+  p.num_rows = num_rows;
+  p.conv_dim = conv_dim;
+  p.history = history;
+  p.window = window;
+  p.align = align_ref(align);
+  ConvTable t{};
+  for (int l = 0; l < num_layers; ++l) {
+    t.l[l].state = layers[l].state;
+    t.l[l].block_stride = layers[l].block_stride;
+    t.l[l].dim_stride = layers[l].dim_stride;
+    t.l[l].token_stride = layers[l].token_stride;
+    t.l[l].num_blocks = layers[l].num_blocks;
+  }
+  void* args[] = {&p, &t};
+  const dim3 grid((unsigned)((conv_dim + kConvThreads - 1) / kConvThreads), (unsigned)num_rows,
+                  (unsigned)num_layers);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&conv_compact_kernel), grid,
+                                       dim3(kConvThreads), args, 0, stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 const char* kda_status_string(kda_status status) {

@@ -255,22 +255,74 @@ def _layer_arrays(layers, pools, state_indices, recs, rows: int):
     return n, Ls, Ps, Rs
 
 
+class Align:
+    """Align mode of the commit: block ids per request row (int32 [rows,
+    width], 0 = null block), the tokens each request had cached before the
+    step (int32 [rows]) and the tokens per block."""
+
+    def __init__(self, block_table: torch.Tensor, num_computed: torch.Tensor, block_size: int):
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be an int32 [rows, width] tensor with unit column stride")
+        _need(num_computed, torch.int32, "num_computed")
+        self.block_table, self.num_computed, self.block_size = block_table, num_computed, int(block_size)
+
+    def c_struct(self, rows: int) -> _lib.KdaAlign:
+        if self.block_table.shape[0] < rows or self.num_computed.numel() < rows:
+            raise ValueError(f"align tables need at least {rows} rows")
+        return _lib.KdaAlign(block_table=self.block_table.data_ptr(),
+                             row_stride=self.block_table.stride(0),
+                             width=self.block_table.shape[1],
+                             num_computed=self.num_computed.data_ptr(),
+                             block_size=self.block_size)
+
+
 def kda_commit_layers(layers, cu_seqlens, pools, state_indices, recs, num_accepted,
-                      record_rows=None, pending=None, eager=None, stream=None) -> None:
+                      record_rows=None, pending=None, eager=None, align: Align | None = None,
+                      stream=None) -> None:
     """kda_commit for every layer in one launch. The layers share the row
-    metadata and the state indices; each has its own pool and records."""
+    metadata and the state indices; each has its own pool and records. With
+    ``align`` the final (and boundary) block of the block table is written
+    instead of the source."""
     _on_gpu(pools[0], cu_seqlens, state_indices, num_accepted, record_rows, pending, eager,
-            *layers, *pools, *recs)
+            *layers, *pools, *recs, *(() if align is None else (align.block_table, align.num_computed)))
     lib = _lib.load()
     _need(cu_seqlens, torch.int32, "cu_seqlens")
     rows = cu_seqlens.numel() - 1
     n, Ls, Ps, Rs = _layer_arrays(layers, pools, state_indices, recs, rows)
+    A = None if align is None else ctypes.byref(align.c_struct(rows))
     st = lib.kda_commit_layers(Ls, Ps, Rs, n, cu_seqlens.data_ptr(), rows,
                                _opt_ptr(record_rows, torch.int32, "record_rows", rows),
                                _opt_ptr(num_accepted, torch.int32, "num_accepted", rows),
                                _opt_ptr(pending, torch.int32, "pending", recs[0].rows),
-                               _opt_ptr(eager, torch.uint8, "eager", rows), _stream(stream))
+                               _opt_ptr(eager, torch.uint8, "eager", rows), A, _stream(stream))
     _lib.check("kda_commit_layers", st)
+
+
+def kda_conv_compact(conv_states, cu_seqlens, state_indices, num_accepted, window: int,
+                     history: int, align: Align | None = None, stream=None) -> None:
+    """The conv-state half of the commit for every layer in one launch.
+    conv_states: 16-bit tensors [blocks, channels, width] (any strides), one
+    per layer; the window after the accepted tokens moves to the front of
+    the final block (and, in align mode, of the boundary block)."""
+    _on_gpu(conv_states[0], cu_seqlens, state_indices, num_accepted, *conv_states,
+            *(() if align is None else (align.block_table, align.num_computed)))
+    lib = _lib.load()
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    rows = cu_seqlens.numel() - 1
+    c0 = conv_states[0]
+    for c in conv_states:
+        if c.element_size() != 2 or c.dim() != 3 or c.shape[1:] != c0.shape[1:]:
+            raise ValueError("conv states must be 16-bit [blocks, channels, width] tensors of one shape")
+    arr = (_lib.KdaConvState * len(conv_states))(*[
+        _lib.KdaConvState(state=c.data_ptr(), block_stride=c.stride(0), dim_stride=c.stride(1),
+                          token_stride=c.stride(2), num_blocks=c.shape[0]) for c in conv_states])
+    A = None if align is None else ctypes.byref(align.c_struct(rows))
+    st = lib.kda_conv_compact(arr, len(conv_states), c0.shape[1], int(history), c0.shape[2],
+                              cu_seqlens.data_ptr(), rows,
+                              _opt_ptr(state_indices, torch.int32, "state_indices", rows),
+                              _opt_ptr(num_accepted, torch.int32, "num_accepted", rows),
+                              int(window), A, _stream(stream))
+    _lib.check("kda_conv_compact", st)
 
 
 def kda_flush_layers(layers, pools, state_indices, rec_prev, pending, record_rows=None,

@@ -200,9 +200,10 @@ def layer_arrays(n=3, over=None):
     return ((_lib.KdaLayer * n)(*Ls), (_lib.KdaPool * n)(*Ps), (_lib.KdaRecords * n)(*Rs), n)
 
 
-def commit_layers(arrs=None, n_rows=2, pending=None, eager=None, acc=A + 0x600000, cu=A):
+def commit_layers(arrs=None, n_rows=2, pending=None, eager=None, acc=A + 0x600000, cu=A, align=None):
     Ls, Ps, Rs, n = arrs or layer_arrays()
-    return _lib.load().kda_commit_layers(Ls, Ps, Rs, n, cu, n_rows, None, acc, pending, eager, None)
+    al = None if align is None else ctypes.byref(align)
+    return _lib.load().kda_commit_layers(Ls, Ps, Rs, n, cu, n_rows, None, acc, pending, eager, al, None)
 
 
 def flush_layers(arrs=None, n_rows=2, pending=A + 0x700000):
@@ -213,10 +214,10 @@ def flush_layers(arrs=None, n_rows=2, pending=A + 0x700000):
 def test_commit_layers_validation():
     lib = _lib.load()
     Ls, Ps, Rs, n = layer_arrays()
-    assert lib.kda_commit_layers(None, Ps, Rs, n, A, 2, None, A, None, None, None) == E["KDA_ERR_NULL"]
+    assert lib.kda_commit_layers(None, Ps, Rs, n, A, 2, None, A, None, None, None, None) == E["KDA_ERR_NULL"]
     assert commit_layers(layer_arrays(1), cu=0) == E["KDA_ERR_NULL"]
     assert commit_layers(layer_arrays(1), acc=0) == E["KDA_ERR_NULL"]
-    assert lib.kda_commit_layers(Ls, Ps, Rs, 0, A, 2, None, A, None, None, None) == E["KDA_ERR_SHAPE"]
+    assert lib.kda_commit_layers(Ls, Ps, Rs, 0, A, 2, None, A, None, None, None, None) == E["KDA_ERR_SHAPE"]
     assert commit_layers(layer_arrays(17)) == E["KDA_ERR_SHAPE"]
     assert commit_layers(layer_arrays(3, {1: {"layer": dict(num_heads=H + 1)}})) == E["KDA_ERR_SHAPE"]
     assert commit_layers(layer_arrays(3, {2: {"rec": dict(window=8)}})) == E["KDA_ERR_SHAPE"]
@@ -245,3 +246,58 @@ def test_flush_layers_validation():
     assert flush_layers(pending=A + 0x30000000) == E["KDA_ERR_ALIAS"]    # pending inside a pool
     assert flush_layers(n_rows=5) == E["KDA_ERR_CAPACITY"]
     assert flush_layers(n_rows=0) == E["KDA_OK"]
+
+
+def align(**kw):
+    d = dict(block_table=A + 0x900000, row_stride=4, width=4, num_computed=A + 0x910000, block_size=16)
+    d.update(kw)
+    return _lib.KdaAlign(**d)
+
+
+def test_commit_layers_align_validation():
+    assert commit_layers(align=align(block_table=0)) == E["KDA_ERR_NULL"]
+    assert commit_layers(align=align(num_computed=0)) == E["KDA_ERR_NULL"]
+    assert commit_layers(align=align(width=0)) == E["KDA_ERR_SHAPE"]
+    assert commit_layers(align=align(block_size=0)) == E["KDA_ERR_SHAPE"]
+    assert commit_layers(align=align(row_stride=3)) == E["KDA_ERR_SHAPE"]
+    # the deferred mode has no align form
+    assert commit_layers(align=align(), pending=A + 0x700000) == E["KDA_ERR_UNSUPPORTED"]
+    assert commit_layers(align=align(), n_rows=0) == E["KDA_OK"]
+
+
+def conv_arrays(n=2, over=None):
+    out = []
+    for l in range(n):
+        d = dict(state=A + 0x40000000 + l * 0x1000000, block_stride=3 * 6, dim_stride=6,
+                 token_stride=1, num_blocks=8)
+        d.update((over or {}).get(l, {}))
+        out.append(_lib.KdaConvState(**d))
+    return (_lib.KdaConvState * n)(*out), n
+
+
+def conv(arrs=None, conv_dim=3, history=3, width=6, n_rows=2, window=4, al=None, cu=A,
+         slots=A + 0x500000, acc=A + 0x600000):
+    cs, n = arrs or conv_arrays()
+    return _lib.load().kda_conv_compact(cs, n, conv_dim, history, width, cu, n_rows, slots, acc,
+                                        window, None if al is None else ctypes.byref(al), None)
+
+
+def test_conv_compact_validation():
+    lib = _lib.load()
+    assert lib.kda_conv_compact(None, 1, 3, 3, 6, A, 2, A, A, 4, None, None) == E["KDA_ERR_NULL"]
+    assert conv(conv_arrays(1, {0: dict(state=0)})) == E["KDA_ERR_NULL"]
+    assert conv(cu=0) == E["KDA_ERR_NULL"]
+    assert conv(slots=0) == E["KDA_ERR_NULL"]
+    assert conv(history=0) == E["KDA_ERR_SHAPE"]
+    assert conv(history=9, width=16) == E["KDA_ERR_SHAPE"]
+    assert conv(width=5) == E["KDA_ERR_SHAPE"]                 # < window + history - 1
+    assert conv(window=0) == E["KDA_ERR_SHAPE"]
+    assert conv(conv_dim=0) == E["KDA_ERR_SHAPE"]
+    assert conv(conv_arrays(65)) == E["KDA_ERR_SHAPE"]
+    assert conv(conv_arrays(1, {0: dict(token_stride=0)})) == E["KDA_ERR_SHAPE"]
+    assert conv(conv_arrays(1, {0: dict(num_blocks=0)})) == E["KDA_ERR_SHAPE"]
+    assert conv(conv_arrays(1, {0: dict(state=A + 0x40000001)})) == E["KDA_ERR_ALIGN"]
+    assert conv(conv_arrays(2, {1: dict(state=A + 0x40000000 + 64)})) == E["KDA_ERR_ALIAS"]
+    assert conv(al=align(width=0)) == E["KDA_ERR_SHAPE"]
+    assert conv(n_rows=70000) == E["KDA_ERR_SHAPE"]
+    assert conv(n_rows=0) == E["KDA_OK"]
