@@ -141,6 +141,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU sample until this much wall time is spent")
+    ap.add_argument("--align", action="store_true",
+                    help="commit in align mode: a block table sends each row's state to other "
+                         "blocks of the pool (decode/deep/ragged workloads)")
     ap.add_argument("--per-layer-commit", action="store_true",
                     help="deferred workload: one kda_commit per layer instead of kda_commit_layers")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -221,8 +224,24 @@ def main():
         kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
                        s["rec"], s["o"], stream=stream)
 
-    def commit(s):
-        kda.kda_commit(layer, cu, s["pool"], si, s["rec"], nacc, stream=stream)
+    align = None
+    if args.align:
+        # rows commit into blocks the sources do not use: c = 2 cached tokens
+        # and 4-token blocks, so a row whose n' exceeds 2 crosses the boundary
+        # at 2 (boundary store into column 0) and ends in column 1
+        free = [b for b in range(1, batch.num_slots) if b not in set(int(x) for x in batch.state_indices)]
+        if len(free) < 2 * B:
+            raise SystemExit("--align needs two free pool blocks per row")
+        bt = np.array(free[:2 * B], np.int32).reshape(B, 2)
+        align = kda.Align(up(bt), up(np.full(B, 2, np.int32)), 4)
+
+    def commit(s, st=None):
+        st = stream if st is None else st
+        if align is None:
+            kda.kda_commit(layer, cu, s["pool"], si, s["rec"], nacc, stream=st)
+        else:
+            kda.kda_commit_layers([layer], cu, [s["pool"]], si, [s["rec"]], nacc, align=align,
+                                  stream=st)
 
     for i in range(args.warmup):
         s = sets[i % len(sets)]
@@ -252,6 +271,9 @@ def main():
 
     n_commit = np.minimum(np.maximum(batch.num_accepted, 0), np.minimum(T, Q))
     vbytes, cbytes = algorithmic_bytes(T, n_commit, valid, H)
+    if align is not None:
+        # the boundary store (after 2 of the 4-token block) of rows with n' > 2
+        cbytes += float(H * STATE_BYTES * np.sum(n_commit[valid] > 2))
     tok_verify = int(T[valid].sum())
     tok_commit = int(n_commit[valid].sum())
     ms_step = total_ms / K
@@ -297,7 +319,7 @@ def main():
         for s in sets:
             kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
                            s["rec"], s["o"], stream=side)
-            kda.kda_commit(layer, cu, s["pool"], si, s["rec"], nacc, stream=side)
+            commit(s, side)
     stream.wait_stream(side)
     torch.cuda.synchronize()
     for s in sets:
@@ -306,7 +328,7 @@ def main():
             cap = torch.cuda.current_stream()
             kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
                            s["rec"], s["o"], stream=cap)
-            kda.kda_commit(layer, cu, s["pool"], si, s["rec"], nacc, stream=cap)
+            commit(s, cap)
         graphs.append(g)
     for i in range(args.warmup):
         graphs[i % len(graphs)].replay()
@@ -353,6 +375,8 @@ def main():
                         f"Q={Q}, bf16 activations, fp32 checkpoints, one layer call per kernel",
             "B": B, "H": H, "K": 128, "V": 128, "T": int(T.max()), "window": Q,
             "verified_tokens_per_step": tok_verify, "committed_tokens_per_step": tok_commit,
+            "commit": "align mode (block table, destinations other than the sources)" if args.align
+                      else "in place",
             "input_sets_rotated": len(sets),
         },
         "roofline": {
@@ -503,6 +527,32 @@ def deferred_leg(args, torch, kda, dev):
     pending.zero_()
     ms_d, kt_vd = timed(deferred_step, K, with_events=True)
 
+    # ---- the conv-state half of the commit for every layer in one launch:
+    # the short convolutions before q, k and v (3 H K channels, bf16), kernel
+    # 4 (history 3), the token axis holding history - 1 + Q columns
+    hist = 3
+    conv_dim = 3 * hk
+    convs = []
+    for _ in range(L):
+        cst = torch.empty((run.num_slots, conv_dim, Q + hist - 1), dtype=torch.bfloat16, device=dev)
+        cst.normal_(generator=gen)
+        convs.append(cst)
+    for s in range(args.warmup):
+        kda.kda_conv_compact(convs, cu, si, nacc[s % S], Q, hist, stream=stream)
+    torch.cuda.synchronize()
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        cev[i][0].record(stream)
+        kda.kda_conv_compact(convs, cu, si, nacc[i % S], Q, hist, stream=stream)
+        cev[i][1].record(stream)
+    torch.cuda.synchronize()
+    conv_us = float(np.mean([a.elapsed_time(b) for a, b in cev])) * 1e3
+    conv_bytes = float(np.mean([
+        L * conv_dim * hist * 2 * 2 * np.sum((np.minimum(np.maximum(run.num_accepted(s), 0), Q) > 0)
+                                            & (run.state_indices > 0))
+        for s in range(S)]))
+    del convs
+
     valid = run.state_indices > 0
     Tv = np.full(B, T)
     be, bvd, bcd = [], [], []
@@ -551,6 +601,8 @@ def deferred_leg(args, torch, kda, dev):
                          "kda_verify_deferred_avg_us": kt_vd * 1e3},
         },
         "deferred_speedup": per_layer_e / per_layer_d,
+        "kda_conv_compact": {"layers": L, "channels": conv_dim, "history": hist, "avg_us": conv_us,
+                             "bytes": conv_bytes, "gbs": conv_bytes / (conv_us * 1e3)},
     }
 
 

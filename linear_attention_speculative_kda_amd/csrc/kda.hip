@@ -866,9 +866,9 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel_layers(Params p, LayerTab
 // accepted tokens the last `history` inputs are columns n' - 1 ..
 // n' + history - 2, and they move to columns 0 .. history - 1 of the final
 // block (in align mode the columns from boundary_len - 1 also go to the
-// boundary block). One thread per (channel, row, layer); a thread reads all
-// of its values before it writes any. The element values are copied as 16-bit
-// patterns.
+// boundary block). A workgroup covers 2048 channels of one (row, layer), 8
+// per thread; a thread reads all of its values before it writes any. The
+// element values are copied as 16-bit patterns.
 constexpr int kMaxConvLayers = 64;
 constexpr int kMaxHistory = 8;
 constexpr int kConvThreads = 256;
@@ -889,8 +889,10 @@ struct ConvTable {
   ConvRef l[kMaxConvLayers];
 };
 
+constexpr int kConvPerThread = 8;   // channels per thread: loads in flight, fewer workgroups
+
+template <int HIST>
 __global__ __launch_bounds__(kConvThreads) void conv_compact_kernel(ConvParams p, ConvTable t) {
-  const int d = blockIdx.x * kConvThreads + threadIdx.x;
   const int row = blockIdx.y;
   const ConvRef& L = t.l[blockIdx.z];
   const int src = p.slots[row];
@@ -907,26 +909,37 @@ __global__ __launch_bounds__(kConvThreads) void conv_compact_kernel(ConvParams p
   if (pl.final_block <= 0 || pl.final_block >= L.num_blocks) return;
   const bool boundary = p.align.bt != nullptr && pl.boundary_block > 0 &&
                         pl.boundary_block < L.num_blocks;
-  if (d >= p.conv_dim) return;
-  const uint16_t* in = L.state + (long long)src * L.block_stride + (long long)d * L.dim_stride;
-  uint16_t fv[kMaxHistory], bv[kMaxHistory];
+  const uint16_t* in = L.state + (long long)src * L.block_stride;
+  uint16_t* fout = L.state + (long long)pl.final_block * L.block_stride;
+  uint16_t* bout = L.state + (long long)pl.boundary_block * L.block_stride;
+  const long long f0 = (long long)(n - 1) * L.token_stride;
+  const long long b0 = (long long)(pl.boundary_len - 1) * L.token_stride;
+  const int d0 = blockIdx.x * kConvThreads * kConvPerThread + threadIdx.x;
+  uint16_t fv[kConvPerThread][HIST], bv[kConvPerThread][HIST];
 #pragma unroll
-  for (int j = 0; j < kMaxHistory; ++j) {
-    if (j < p.history) {
-      fv[j] = in[(long long)(n - 1 + j) * L.token_stride];
-      if (boundary) bv[j] = in[(long long)(pl.boundary_len - 1 + j) * L.token_stride];
+  for (int u = 0; u < kConvPerThread; ++u) {
+    const int d = d0 + u * kConvThreads;
+    if (d < p.conv_dim) {
+      const uint16_t* x = in + (long long)d * L.dim_stride;
+#pragma unroll
+      for (int j = 0; j < HIST; ++j) {
+        fv[u][j] = x[f0 + (long long)j * L.token_stride];
+        if (boundary) bv[u][j] = x[b0 + (long long)j * L.token_stride];
+      }
     }
   }
-  if (boundary) {
-    uint16_t* out = L.state + (long long)pl.boundary_block * L.block_stride + (long long)d * L.dim_stride;
 #pragma unroll
-    for (int j = 0; j < kMaxHistory; ++j)
-      if (j < p.history) out[(long long)j * L.token_stride] = bv[j];
+  for (int u = 0; u < kConvPerThread; ++u) {
+    const int d = d0 + u * kConvThreads;
+    if (d < p.conv_dim) {
+      const long long off = (long long)d * L.dim_stride;
+#pragma unroll
+      for (int j = 0; j < HIST; ++j)
+        if (boundary) bout[off + (long long)j * L.token_stride] = bv[u][j];
+#pragma unroll
+      for (int j = 0; j < HIST; ++j) fout[off + (long long)j * L.token_stride] = fv[u][j];
+    }
   }
-  uint16_t* out = L.state + (long long)pl.final_block * L.block_stride + (long long)d * L.dim_stride;
-#pragma unroll
-  for (int j = 0; j < kMaxHistory; ++j)
-    if (j < p.history) out[(long long)j * L.token_stride] = fv[j];
 }
 
 // ------------------------------------------------------------------- host --
@@ -1467,10 +1480,21 @@ kda_status kda_conv_compact(const kda_conv_state* layers, int32_t num_layers, in
     t.l[l].num_blocks = layers[l].num_blocks;
   }
   void* args[] = {&p, &t};
-  const dim3 grid((unsigned)((conv_dim + kConvThreads - 1) / kConvThreads), (unsigned)num_rows,
+  const void* fn = nullptr;
+  switch (history) {
+    case 1: fn = reinterpret_cast<const void*>(&conv_compact_kernel<1>); break;
+    case 2: fn = reinterpret_cast<const void*>(&conv_compact_kernel<2>); break;
+    case 3: fn = reinterpret_cast<const void*>(&conv_compact_kernel<3>); break;
+    case 4: fn = reinterpret_cast<const void*>(&conv_compact_kernel<4>); break;
+    case 5: fn = reinterpret_cast<const void*>(&conv_compact_kernel<5>); break;
+    case 6: fn = reinterpret_cast<const void*>(&conv_compact_kernel<6>); break;
+    case 7: fn = reinterpret_cast<const void*>(&conv_compact_kernel<7>); break;
+    default: fn = reinterpret_cast<const void*>(&conv_compact_kernel<8>); break;
+  }
+  const int per_block = kConvThreads * kConvPerThread;
+  const dim3 grid((unsigned)((conv_dim + per_block - 1) / per_block), (unsigned)num_rows,
                   (unsigned)num_layers);
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&conv_compact_kernel), grid,
-                                       dim3(kConvThreads), args, 0, stream);
+  const hipError_t e = hipLaunchKernel(fn, grid, dim3(kConvThreads), args, 0, stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
