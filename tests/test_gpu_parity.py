@@ -264,3 +264,30 @@ def test_full_size_sampled_parity(name):
 def test_full_size_commit_bitexact(name):
     batch = make_batch(name)
     commit_bitexact_vs_recurrent(batch, full_pool(batch), batch.num_accepted)
+
+
+@pytest.mark.parametrize("name", ["decode", "deep", "ragged"])
+def test_verify_outputs_match_recurrent_outputs(name):
+    """kda_verify (the chunked form against the checkpoint) and kda_recurrent
+    (the per-token loop) compute the same window from the same checkpoints:
+    every output within the output tolerance (the sums run in different
+    orders, so not bit for bit)."""
+    batch = make_batch(name)
+    say(f"verify vs recurrent outputs: {name}")
+    B, H, Q = batch.num_rows, batch.H, batch.Q
+    pool_np = batch.initial_pool()
+    if not pool_np.any():   # checkpoints made by a prefill: use N(0, 0.02) states instead
+        rng = np.random.default_rng(17)
+        for s in batch.state_indices[batch.state_indices > 0]:
+            pool_np[s] = rng.standard_normal(pool_np.shape[1:], dtype=np.float32) * np.float32(0.02)
+    ntok = batch.tokens.num_tokens
+    layer = dev_layer(batch)
+    tok = DevTokens(batch.tokens)
+    cu, si = to_dev(batch.cu_seqlens), to_dev(batch.state_indices)
+    pool = to_dev(pool_np)
+    o_v = torch.zeros((ntok, H, 128), dtype=torch.bfloat16, device=DEV)
+    o_r = torch.zeros_like(o_v)
+    kda.kda_verify(layer, *tok.args(), cu, pool, si, dev_records(B, H, Q), o_v)
+    kda.kda_recurrent(layer, *tok.args(), cu, pool.clone(), si, o_r)
+    torch.cuda.synchronize()
+    check_o(bits_host(o_v), bits_host(o_r), what=f"{name}: verify o vs recurrent o")
