@@ -747,8 +747,9 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   // loads to the outputs. A control-flow join between the state loads and
   // their first use lets the compiler copy the state registers there, which
   // waits for the whole tile before the token staging can start.
-  if constexpr (MODE == kVerify) {
-    if (chunk) {
+  // (kda_verify_deferred takes it too for rows with nothing to fold.)
+  if constexpr (MODE == kVerify || MODE == kDeferred) {
+    if (chunk && nfold == 0) {
       Raw<BV> raw;
       stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
       __builtin_amdgcn_sched_barrier(0);
