@@ -279,13 +279,10 @@ struct Stage {
 // over tokens s+1..t, both diagonal over key channels):
 //   al[t] = Gamma_t k^_t,  ga[t] = Gamma_t q^_t,
 //   M[t][s] = k^_s . P(s,t) k^_t  (s < t),   N[t][s] = k^_s . P(s,t) q^_t.
-//   w[s] = P(s,m) k^_s and gm = Gamma_m for the state after the chunk.
 template <int BV, int NT>
 struct StageChunk : Stage<BV, NT> {
   float al[NT][KD];
   float ga[NT][KD];
-  float w[NT][KD];
-  float gm[KD];
   float M[NT][NT];
   float N[NT][NT];
 };
@@ -491,14 +488,13 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
 //   u_t = beta_t (v_t - a_t - sum_{s<t} M[t][s] u_s)
 //   o_t = b_t + sum_{s<=t} N[t][s] u_s
 // which is the per-token loop's math (decay, delta rule, update, output)
-// with 2m dot products per value row instead of 4m passes over it. With
-// `more`, the state is advanced to the chunk's end for the next chunk:
-//   S_m = Gamma_m S0 + sum_s P(s,m) k^_s u_s^T.
+// with 2m dot products per value row instead of 4m passes over it. Windows
+// longer than one chunk run through the per-token loop.
 //
 // coef_phase: the per-chunk vectors and coefficients, from the staged k^,
 // q^, exp(g), by 256 threads (c.tid 0..255; c.hw and c.l32 relative to them).
 template <int BV, int TMAX, int NT>
-__device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c, int T, bool more) {
+__device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c, int T) {
   // Decayed vectors: threads 0..127, one key channel each (all of the
   // channel's staged values are read first, then a short product chain).
   if (c.tid < KD) {
@@ -519,17 +515,6 @@ __device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c,
         gam = gam * dd[t];
         st.al[t][ch] = gam * kk[t];
         st.ga[t][ch] = gam * qq[t];
-      }
-    }
-    if (more) {
-      st.gm[ch] = gam;
-      float pr = 1.0f;
-#pragma unroll
-      for (int t = TMAX - 1; t >= 0; --t) {
-        if (t < T) {
-          st.w[t][ch] = pr * kk[t];
-          pr = pr * dd[t];
-        }
       }
     }
   }
@@ -602,64 +587,43 @@ __device__ __forceinline__ void chunk_dots(const float (&S)[R][16], const StageC
   }
 }
 
-// chunk_recur: the T x T triangular recurrence per value row, the outputs
-// (lane p8 of the group stores token p8's output, to o[tok0 + p8]) and, with
-// `more`, the state at the chunk's end.
+// chunk_recur: the T x T triangular recurrence per value row and the
+// outputs (lane p8 of the group stores token p8's output, to o[tok0 + p8]).
 template <int R, int BV, int TMAX, int NT>
-__device__ __forceinline__ void chunk_recur(float (&S)[R][16], const StageChunk<BV, NT>& st,
-                                            const Params& p, const Ctx& c, int T, long long tok0,
-                                            bool more, const float (&a)[R][TMAX],
-                                            const float (&b)[R][TMAX]) {
-  float u[R][TMAX];
+__device__ __forceinline__ void chunk_recur(const StageChunk<BV, NT>& st, const Params& p,
+                                            const Ctx& c, int T, long long tok0,
+                                            const float (&a)[R][TMAX], const float (&b)[R][TMAX]) {
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     const int vloc = row_in_tile(rr, c);
+    float u[TMAX];
     float mine = 0.0f;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
         float x = st.vt[t][vloc] - a[rr][t];
 #pragma unroll
-        for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[rr][s], x);
-        u[rr][t] = st.bt[t] * x;
+        for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[s], x);
+        u[t] = st.bt[t] * x;
         float y = b[rr][t];
 #pragma unroll
-        for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[rr][s], y);
+        for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[s], y);
         if (c.p8 == t) mine = y;
       }
     }
     if (c.p8 < T)
       p.o[((tok0 + c.p8) * c.H + c.head) * KD + c.tile * BV + vloc] = f32_to_bf16(mine);
   }
-  if (more) {
-    float g16[16];
-    lds_row16(st.gm, c.p8, g16);
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) S[rr][e] = S[rr][e] * g16[e];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (t < T) {
-        lds_row16(st.w[t], c.p8, g16);
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) S[rr][e] = fmaf(g16[e], u[rr][t], S[rr][e]);
-      }
-    }
-  }
 }
 
 template <int R, int BV, int TMAX, int NT>
-__device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, NT>& st,
-                                             const Params& p, const Ctx& c, int T,
-                                             long long tok0, bool more) {
-  coef_phase<BV, TMAX, NT>(st, c, T, more);
+__device__ __forceinline__ void chunk_verify(const float (&S)[R][16], StageChunk<BV, NT>& st,
+                                             const Params& p, const Ctx& c, int T, long long tok0) {
+  coef_phase<BV, TMAX, NT>(st, c, T);
   lds_barrier();
   float a[R][TMAX], b[R][TMAX];
   chunk_dots<R, BV, TMAX, NT>(S, st, c, T, a, b);
-  chunk_recur<R, BV, TMAX, NT>(S, st, p, c, T, tok0, more, a, b);
+  chunk_recur<R, BV, TMAX, NT>(st, p, c, T, tok0, a, b);
 }
 
 // ------------------------------------------------------------------ kernel --
@@ -758,7 +722,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       __builtin_amdgcn_sched_barrier(0);
       stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0, false);
       lds_barrier();
-      chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos, false);
+      chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos);
       // the records last: stores issued behind the state loads would make
       // later register reuse wait for those loads
       store_records<BV>(raw, p, c, 0);
@@ -804,7 +768,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
         lds_barrier();
         stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0);
         lds_barrier();
-        chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos, false);
+        chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos);
         return;
       }
     }
