@@ -6,32 +6,37 @@
 // a fp32 state S[K, V]; per token decay the key channels by exp(g), delta rule
 // u = beta * (v - S^T k^), rank-1 update S += k^ u^T, output o = S^T q^.
 //
-// Kernel design (one kernel template serves the four calls):
+// Kernel design (one kernel body serves the recurrent, verify, commit and
+// deferred calls, single- or multi-layer):
 //  * One workgroup of 256 threads (4 waves) per (request row, head, V-tile of
-//    BV = 32*R value rows). The fp32 K x BV state tile lives in VGPRs for the
-//    whole token loop: a group of 8 adjacent lanes owns one value row; each
-//    lane holds 16 key channels of it (4 chunks of 4 consecutive channels,
-//    chunk j at j*32 + 4*(lane%8)), so one 128-bit load per chunk and the 8
-//    lanes of a group read 128 contiguous bytes. Each lane holds R rows.
+//    BV = 32*R value rows). The fp32 K x BV state tile lives in VGPRs: a group
+//    of 8 adjacent lanes owns one value row; each lane holds 16 key channels
+//    of it (4 chunks of 4 consecutive channels, chunk j at j*32 + 4*(lane%8)),
+//    so one 128-bit load per chunk and the 8 lanes of a group read 128
+//    contiguous bytes. Each lane holds R rows.
 //  * The per-token vectors shared by all rows (k^, q^, exp(g), beta and the
 //    tile's slice of v) are computed once per workgroup, 8 tokens at a time,
-//    by half-waves (one token each, 4 channels per lane) into LDS. The state
-//    tile's loads are issued before this staging so that they are in flight
-//    meanwhile.
-//  * The two reductions over K per token and row (S^T k^ and S^T q^) are
-//    16-term in-lane FMA chains plus a 3-step DPP butterfly across the 8
-//    lanes of the group (quad_perm 1032, quad_perm 2301, row_half_mirror).
-//    A butterfly adds the same two operands in every lane, so all 8 lanes
-//    get the same bits.
-//  * No MFMA: per token the work is two matrix-vector products and a rank-1
-//    update of a 64 KiB state that is read once and written at most once, so
-//    the path is bound by HBM bandwidth, not by a dense contraction.
-//  * Every call runs the same per-token code with the same lane layout, so a
-//    commit of n records gives the bits of the plain recurrence over the same
-//    n tokens. The build uses -ffp-contract=off: every FMA is an explicit
-//    fmaf, nothing is contracted or reassociated by the compiler.
+//    by half-waves (one token each, 4 channels per lane) into LDS. The token
+//    loads go out first and the state tile's right after, so the staging runs
+//    while the tile is in flight; barriers wait for LDS operations only.
+//  * Commit, recurrence and the deferred fold step the state token by token
+//    (two reductions over K per token and row: 16-term in-lane FMA chains plus
+//    a 3-step DPP butterfly across the 8 lanes of the group, which gives all 8
+//    lanes the same bits). Every one of them runs the same per-token code with
+//    the same lane layout, so a commit of n records gives the bits of the
+//    plain recurrence over the same n tokens.
+//  * Verify computes its window in chunked form against the checkpoint: 2T
+//    dot products per value row and a T x T triangular recurrence, no state
+//    stepping and no state write.
+//  * No MFMA: the work per state element is a handful of FMAs against a state
+//    that is read once and written at most once; the path is bound by HBM
+//    bandwidth (measured: the verify's dot products on the matrix cores ran no
+//    faster).
+//  * -ffp-contract=off: every FMA is an explicit fmaf, nothing is contracted
+//    or reassociated by the compiler.
 //  * Every index read from device memory (cu_seqlens, slots, record rows,
-//    accepted counts, pending counts) is range-checked before use.
+//    accepted and pending counts, block tables) is range-checked before use.
+// The conv-state compaction of the commit is a separate small copy kernel.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
