@@ -73,13 +73,19 @@ def kernel_key(name: str) -> str:
     for mode, call in (("0", "kda_recurrent"), ("2", "kda_commit"), ("3", "kda_verify_deferred")):
         if f"kda_kernel<{mode}," in name:
             return call
+    for mode, call in (("2", "kda_commit_layers"), ("3", "kda_flush_layers")):
+        if f"kda_kernel_layers<{mode}," in name:
+            return call
+    if "conv_compact_kernel" in name:
+        return "kda_conv_compact"
     return name
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str) -> dict:
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> dict:
     """Per-dispatch HBM traffic of each library kernel from two rocprofv3
-    --pmc runs of this benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per
-    dispatch). Each counter is calibrated on the plain 1 GiB copy that the
+    --pmc runs of this benchmark on one workload (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch), merged into the summary file under that
+    workload. Each counter is calibrated on the plain 1 GiB copy that the
     benchmark times: its dispatches write exactly 1 GiB, so
     factor = 1 GiB / (what the counter reads for them)."""
     def load(d, counter):
@@ -99,7 +105,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> dict:
         raise SystemExit("no 1 GiB copy dispatches found to calibrate the counters")
     f_scale = copy_kib / float(np.median(copy_f))
     w_scale = copy_kib / float(np.median(copy_w))
-    out = {"source_sha256": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+    out = {"fetch_scale": f_scale, "write_scale": w_scale,
            "copy_fetch_kib": float(np.median(copy_f)), "copy_write_kib": float(np.median(copy_w)),
            "kernels": {}}
     by = {}
@@ -113,12 +119,21 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> dict:
         fk, wk = float(np.median(d["fetch"])), float(np.median(d["write"]))
         out["kernels"][key] = {"fetch_kib": fk, "write_kib": wk, "dispatches": len(d["fetch"]),
                                "traffic_bytes": (fk * f_scale + wk * w_scale) * 1024}
-    return out
+    try:
+        with open(TRAFFIC_FILE) as f:
+            summary = json.load(f)
+    except (OSError, ValueError):
+        summary = {}
+    if summary.get("source_sha256") != source_hash():
+        summary = {"source_sha256": source_hash(), "workloads": {}}
+    summary.setdefault("workloads", {})[workload] = out
+    return summary
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, or None when there is none or the kernel source changed
+    since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -126,7 +141,7 @@ def measured_traffic(kernel: str):
         return None
     if t.get("source_sha256") != source_hash():
         return None
-    k = t.get("kernels", {}).get(kernel)
+    k = t.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
     return None if k is None else k["traffic_bytes"]
 
 
@@ -147,14 +162,15 @@ def parse():
     ap.add_argument("--per-layer-commit", action="store_true",
                     help="deferred workload: one kda_commit per layer instead of kda_commit_layers")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
+                    help="merge two rocprofv3 --pmc runs of --workload into profiles/traffic.json "
+                         "and exit")
     return ap.parse_args()
 
 
 def main():
     args = parse()
     if args.summarize_pmc:
-        out = summarize_pmc(*args.summarize_pmc)
+        out = summarize_pmc(*args.summarize_pmc, args.workload)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(out, f, indent=1)
@@ -342,20 +358,7 @@ def main():
     torch.cuda.synchronize()
     ms_step_graph = g_start.elapsed_time(g_end) / K
 
-    # ---- achievable copy bandwidth on this GPU (context for the peak)
-    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 10 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e6)
-    del src, dst
+    copy_gbs = device_copy_gbs(torch, stream)
 
     result = {
         "metric": "KDA verify+commit tokens/s and achieved HBM GB/s vs peak (B=64,H=32,T=4)",
@@ -386,7 +389,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": kernels[dom]["gbs"] / PEAK_HBM_GBS,
-            "traffic": measured_traffic(dom),
+            "traffic": measured_traffic(dom, args.workload),
         },
         "kernels": kernels,
         "kda_verify_without_preceding_commit": verify_isolated,
@@ -405,6 +408,26 @@ def main():
         result["cpu_baseline"] = cpu_baseline(batch, args.cpu_rows, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def device_copy_gbs(torch, stream) -> float:
+    """The achievable copy bandwidth on this GPU (context for the peak): a
+    plain 1 GiB device copy, timed 10 times; also what the counter
+    calibration of --summarize-pmc finds in a profile of this benchmark."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=stream.device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 10 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e6)
+    del src, dst
+    return gbs
 
 
 def deferred_bytes(T, n_prev, eager_prev, n_now, eager_now, valid, H):
@@ -547,6 +570,7 @@ def deferred_leg(args, torch, kda, dev):
         cev[i][1].record(stream)
     torch.cuda.synchronize()
     conv_us = float(np.mean([a.elapsed_time(b) for a, b in cev])) * 1e3
+    copy_gbs = device_copy_gbs(torch, stream)
     conv_bytes = float(np.mean([
         L * conv_dim * hist * 2 * 2 * np.sum((np.minimum(np.maximum(run.num_accepted(s), 0), Q) > 0)
                                             & (run.state_indices > 0))
@@ -590,7 +614,7 @@ def deferred_leg(args, torch, kda, dev):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": gbs_vd / PEAK_HBM_GBS,
-            "traffic": measured_traffic("kda_verify_deferred"),
+            "traffic": measured_traffic("kda_verify_deferred", "deferred"),
         },
         "flows": {
             "eager": {"ms_per_layer_step": per_layer_e, "bytes_per_layer_step": b_eager,
@@ -603,6 +627,7 @@ def deferred_leg(args, torch, kda, dev):
         "deferred_speedup": per_layer_e / per_layer_d,
         "kda_conv_compact": {"layers": L, "channels": conv_dim, "history": hist, "avg_us": conv_us,
                              "bytes": conv_bytes, "gbs": conv_bytes / (conv_us * 1e3)},
+        "copy_gbs_measured": copy_gbs,
     }
 
 
