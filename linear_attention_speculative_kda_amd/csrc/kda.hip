@@ -25,6 +25,9 @@
 //    lanes the same bits). Every one of them runs the same per-token code with
 //    the same lane layout, so a commit of n records gives the bits of the
 //    plain recurrence over the same n tokens.
+//  * A commit that defers (only the eager rows replay now) runs over a list of
+//    the rows with work, built in every workgroup of a grid sized to the
+//    resident capacity, instead of one workgroup per (row, head, tile).
 //  * Verify computes its window in chunked form against the checkpoint: 2T
 //    dot products per value row and a T x T triangular recurrence, no state
 //    stepping and no state write.
@@ -424,7 +427,7 @@ __device__ __forceinline__ void stage_compute(Stage<BV, NT>& st, const Raw<BV>& 
                                               const Ctx& c, bool fold, int c0, bool records = true) {
   constexpr int VPL = BV / 32;
   if (!x.active) return;
-  const int hw = c.hw, l32 = c.l32, j = c0 + hw;
+  const int hw = c.hw, l32 = c.l32;
   float kx[4], gx[4];
   unpack4(x.k, kx);
   unpack4(x.g, gx);
@@ -634,6 +637,25 @@ __device__ __forceinline__ void chunk_verify(const float (&S)[R][16], StageChunk
 // ------------------------------------------------------------------ kernel --
 
 // One workgroup's work: (row, head, tile) from its logical block index b.
+// The commit's view of a request row: its span length T (a malformed span
+// counts as empty), n' = the accepted count clamped to [0, min(T, Q)], and
+// whether the row replays its records in this call (always, unless the call
+// defers: then only the rows marked eager).
+__device__ __forceinline__ int commit_span(const Params& p, int row) {
+  const int bos = p.cu[row];
+  const int T = p.cu[row + 1] - bos;
+  return (bos < 0 || T < 0) ? 0 : T;
+}
+__device__ __forceinline__ int commit_count(const Params& p, int row, int T) {
+  int n = p.num_accepted[row];
+  n = n < 0 ? 0 : n;
+  n = n < T ? n : T;
+  return n < p.Q ? n : p.Q;
+}
+__device__ __forceinline__ bool commit_now(const Params& p, int row) {
+  return p.pending == nullptr || (p.eager != nullptr && p.eager[row] != 0);
+}
+
 template <int MODE, int R, int TMAX>
 __device__ __forceinline__ void kda_block(const Params& p, int b) {
   constexpr int BV = R * NWAVES * 8;   // value rows per workgroup
@@ -673,10 +695,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   float* bbase = nullptr;   // align mode: where the boundary state goes, after blen records
   int blen = 0;
   if (MODE == kCommit) {
-    int n = p.num_accepted[row];
-    n = n < 0 ? 0 : n;
-    n = n < T ? n : T;
-    n = n < p.Q ? n : p.Q;
+    const int n = commit_count(p, row, T);
     bool final_ok = true;
     if (p.align.bt && slot_ok && n > 0) {
       const Plan pl = commit_plan_row(p.align, row, n, slot);
@@ -689,9 +708,8 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       }
     }
     const bool valid = slot_ok && n > 0 && c.ri > 0 && final_ok;
-    bool now = true;
+    const bool now = commit_now(p, row);
     if (p.pending) {
-      now = p.eager != nullptr && p.eager[row] != 0;
       if (!p.pending_skip && c.ri > 0 && c.head == 0 && c.tile == 0 && c.tid == 0)
         p.pending[c.ri - 1] = now ? 0 : (valid ? n : 0);
     }
@@ -805,12 +823,7 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
 // The same work for several layers in one grid: logical block b belongs to
 // layer b / layer_blocks, whose pool, records and gate parameters replace
 // the shared ones.
-template <int MODE, int R, int TMAX>
-__global__ __launch_bounds__(NTHREADS) void kda_kernel_layers(Params p, LayerTable t) {
-  int b = logical_block(p.total_blocks);
-  const int l = b / p.layer_blocks;
-  b -= l * p.layer_blocks;
-  const LayerRef& L = t.l[l];
+__device__ __forceinline__ void apply_layer(Params& p, const LayerRef& L) {
   p.a_log = L.a_log;
   p.g_bias = L.g_bias;
   p.scale = L.scale;
@@ -821,11 +834,85 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel_layers(Params p, LayerTab
   p.state = L.state;
   p.rk = L.rk; p.rv = L.rv; p.rg = L.rg; p.rb = L.rb;
   p.pk = L.pk; p.pv = L.pv; p.pg = L.pg; p.pb = L.pb;
+}
+
+template <int MODE, int R, int TMAX>
+__global__ __launch_bounds__(NTHREADS) void kda_kernel_layers(Params p, LayerTable t) {
+  int b = logical_block(p.total_blocks);
+  const int l = b / p.layer_blocks;
+  b -= l * p.layer_blocks;
+  apply_layer(p, t.l[l]);
   // pending is one array per request row, shared by the layers (they share
   // the state indices, so every layer would write the same counts): layer 0
   // writes it
   if (l != 0) p.pending_skip = 1;
   kda_block<MODE, R, TMAX>(p, b);
+}
+
+// Commit over a list of rows. A deferring commit replays records for the
+// eager rows only, and an eager one skips the rows with nothing accepted; a
+// workgroup per (row, layer, head, tile) would then spend most of the launch
+// starting workgroups that only read the row metadata and exit. Here a grid
+// sized to the resident capacity first builds, in every workgroup alike,
+// the list of rows that may replay (row order: one ballot per 64 rows, then
+// prefix counts), and then takes every G-th (row, layer, head, tile) unit of
+// that list; each unit is the ordinary commit workgroup body, which decides
+// for itself (the list is a superset: the slot's upper bound and the align
+// blocks are checked per layer there). Workgroup 0 writes the pending
+// counts of all rows, as the first layer's workgroups do in the full grid.
+constexpr int kListRows = 2048;
+
+template <int R>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(R == 1 ? 5 : 1)))
+void kda_commit_list(Params p, LayerTable t, int num_layers) {
+  __shared__ unsigned long long mask[kListRows / 64];
+  __shared__ unsigned short list[kListRows];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nchunks = (p.num_rows + 63) >> 6;
+  const bool write_pending = p.pending != nullptr && blockIdx.x == 0;
+  const int slots0 = t.l[0].num_slots;
+  for (int k = wave; k < nchunks; k += NWAVES) {
+    const int row = k * 64 + lane;
+    bool work = false;
+    if (row < p.num_rows) {
+      const int T = commit_span(p, row);
+      const int n = commit_count(p, row, T);
+      const int slot = p.slots[row];
+      const int r = p.record_rows ? p.record_rows[row] : row;
+      const int ri = (r >= 0 && r < p.rec_rows) ? r + 1 : 0;
+      const bool now = commit_now(p, row);
+      work = now && n > 0 && slot > 0 && ri > 0;
+      if (write_pending && ri > 0) {
+        const bool valid = slot > 0 && slot < slots0 && n > 0;   // as the first layer sees it
+        p.pending[ri - 1] = now ? 0 : (valid ? n : 0);
+      }
+    }
+    const unsigned long long m = __ballot(work);
+    if (lane == 0) mask[k] = m;
+  }
+  lds_barrier();
+  int count = 0;
+  for (int k = 0; k < nchunks; ++k) {
+    const unsigned long long m = mask[k];
+    if ((k & (NWAVES - 1)) == wave && ((m >> lane) & 1ull))
+      list[count + __popcll(m & ((1ull << lane) - 1ull))] = (unsigned short)(k * 64 + lane);
+    count += __popcll(m);
+  }
+  lds_barrier();
+  const int per_layer = p.H * p.tiles;
+  const int per_row = num_layers * per_layer;
+  const long long units = (long long)count * per_row;
+  const int G = gridDim.x;
+  p.pending_skip = 1;
+  for (long long u = logical_block(G); u < units; u += G) {
+    const int e = (int)(u / per_row);
+    int rem = (int)(u - (long long)e * per_row);
+    const int l = rem / per_layer;
+    rem -= l * per_layer;
+    apply_layer(p, t.l[l]);
+    kda_block<kCommit, R, CH>(p, (int)list[e] * per_layer + rem);
+  }
 }
 
 // ------------------------------------------------------- conv compaction --
@@ -1124,6 +1211,79 @@ kda_status launch_layers(Params& p, LayerTable& t, int num_layers, hipStream_t s
   }
 }
 
+// The row-list commit: the default when the call defers (most rows then
+// have nothing to replay now), else the full grid. KDA_COMMIT_LIST=0 / 1
+// forces the full grid / the list (read once). Calls with more rows than
+// the list holds take the full grid.
+bool commit_by_list(const Params& p) {
+  static int forced = -2;
+  if (forced == -2) {
+    forced = -1;
+    const char* env = getenv("KDA_COMMIT_LIST");
+    if (env && (env[0] == '0' || env[0] == '1') && env[1] == 0) forced = env[0] - '0';
+  }
+  if (p.num_rows > kListRows) return false;
+  return forced >= 0 ? forced == 1 : p.pending != nullptr;
+}
+
+// Workgroups of kda_commit_list<R> resident at once on the current device
+// (compute units x workgroups per unit), queried once per device.
+template <int R>
+int list_capacity() {
+  constexpr int kDevices = 64;
+  static int cap[kDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kDevices && cap[dev] > 0) return cap[dev];
+  int occ = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &occ, reinterpret_cast<const void*>(&kda_commit_list<R>), NTHREADS, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int c = occ * cus;
+  if (dev < kDevices) cap[dev] = c;
+  return c;
+}
+
+template <int R>
+kda_status launch_list_r(Params& p, LayerTable& t, int num_layers, hipStream_t stream) {
+  p.tiles = KD / (32 * R);
+  const long long full = (long long)p.num_rows * p.H * p.tiles * num_layers;
+  long long grid = list_capacity<R>();
+  if (grid < 1) return KDA_ERR_LAUNCH;
+  if (grid > full) grid = full;
+  p.total_blocks = (int)grid;
+  void* args[] = {&p, &t, &num_layers};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_commit_list<R>),
+                                       dim3((unsigned)grid), dim3(NTHREADS), args, 0, stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status launch_list(Params& p, LayerTable& t, int num_layers, hipStream_t stream) {
+  switch (tile_rows_for(kCommit, (long long)p.num_rows * p.H)) {
+    case 32: return launch_list_r<1>(p, t, num_layers, stream);
+    case 64: return launch_list_r<2>(p, t, num_layers, stream);
+    default: return launch_list_r<4>(p, t, num_layers, stream);
+  }
+}
+
+// The one-entry layer table of a single-layer call.
+LayerTable single_layer(const Params& p) {
+  LayerTable t{};
+  LayerRef& r = t.l[0];
+  r.a_log = p.a_log;
+  r.g_bias = p.g_bias;
+  r.scale = p.scale;
+  r.lower_bound = p.lower_bound;
+  r.has_lb = p.has_lb;
+  r.num_slots = p.num_slots;
+  r.slot_stride = p.slot_stride;
+  r.state = p.state;
+  r.rk = p.rk; r.rv = p.rv; r.rg = p.rg; r.rb = p.rb;
+  r.pk = p.pk; r.pv = p.pv; r.pg = p.pg; r.pb = p.pb;
+  return t;
+}
+
 template <int MODE>
 kda_status launch(Params& p, hipStream_t stream) {
   if ((MODE == kVerify || MODE == kDeferred) && p.Q <= 4) return launch_t<MODE, 4>(p, stream);
@@ -1306,6 +1466,10 @@ kda_status kda_commit(const kda_layer* layer, const int32_t* cu_seqlens, int32_t
   p.num_accepted = num_accepted;
   p.pending = pending;
   p.eager = eager;
+  if (commit_by_list(p)) {
+    LayerTable t = single_layer(p);
+    return launch_list(p, t, 1, stream);
+  }
   return launch<kCommit>(p, stream);
 }
 
@@ -1380,6 +1544,7 @@ kda_status kda_commit_layers(const kda_layer* layers, const kda_pool* pools,
   p.align = align_ref(align);
   LayerTable t{};
   fill_layer_table(t, layers, pools, recs, num_layers, false);
+  if (commit_by_list(p)) return launch_list(p, t, num_layers, stream);
   return launch_layers<kCommit>(p, t, num_layers, stream);
 }
 

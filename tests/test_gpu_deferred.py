@@ -136,3 +136,15 @@ def test_deferred_full_size():
     say(f"case deferred B={run.B} H={run.H} layers={run.layers} steps={run.steps}")
     res = gpu_flows(run)
     compare(run, *res, sample=[(0, [0, 17, 300]), (5, [42, 511]), (7, [9])])
+
+
+@pytest.mark.parametrize("B", [2048, 2049])
+def test_deferred_row_list_capacity(B):
+    """A deferring commit builds the list of rows that replay now; 2048 rows
+    is the most the list holds (every 64-row chunk in use), 2049 takes the
+    full grid. Both must match the eager flow bitwise and the oracle on the
+    first and last rows."""
+    run = make_deferred(B=B, H=1, layers=2, steps=3)
+    say(f"case deferred row list B={B} H=1 layers=2 steps=3")
+    res = gpu_flows(run)
+    compare(run, *res, sample=[(1, [0, B - 1])])
