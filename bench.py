@@ -76,6 +76,8 @@ def kernel_key(name: str) -> str:
     for mode, call in (("2", "kda_commit_layers"), ("3", "kda_flush_layers")):
         if f"kda_kernel_layers<{mode}," in name:
             return call
+    if "kda_commit_list" in name:
+        return "kda_commit_deferring"     # a commit with pending counts, by row list
     if "conv_compact_kernel" in name:
         return "kda_conv_compact"
     return name
@@ -358,6 +360,10 @@ def main():
     torch.cuda.synchronize()
     ms_step_graph = g_start.elapsed_time(g_end) / K
 
+    deferred = None if align is not None else decode_deferred_flow(
+        args, torch, kda, layer, sets, cu, si, nacc, stream, T, n_commit, valid, H, B, Q, dev,
+        tok_verify)
+
     copy_gbs = device_copy_gbs(torch, stream)
 
     result = {
@@ -403,11 +409,102 @@ def main():
         "verify_tokens_per_s": tok_verify / (v_ms * 1e-3),
         "copy_gbs_measured": copy_gbs,
     }
+    if deferred is not None:
+        result["deferred_flow"] = deferred
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(batch, args.cpu_rows, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def decode_deferred_flow(args, torch, kda, layer, sets, cu, si, nacc, stream, T, n_commit, valid,
+                         H, B, Q, dev, tok_verify):
+    """The same step in the deferred flow: kda_verify_deferred folds the
+    records the previous step of the same input set accepted into the
+    checkpoint (and stores it) while it verifies; the commit then only
+    records this step's accepted counts as pending (no eager rows). Two
+    record buffers per set alternate. Timed like the eager step: events
+    around eager launches for the kernels, HIP graphs for the step."""
+    for s in sets:
+        s["recs"] = [s["rec"], kda.allocate_records(B, H, Q, dev)]
+        s["pending"] = torch.zeros(B, dtype=torch.int32, device=dev)
+    nsets = len(sets)
+
+    def dstep(c, st, ev=None):
+        s = sets[c % nsets]
+        par = (c // nsets) % 2
+        if ev is not None:
+            ev[0].record(st)
+        kda.kda_verify_deferred(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
+                                s["recs"][1 - par], s["pending"], s["recs"][par], s["o"], stream=st)
+        if ev is not None:
+            ev[1].record(st)
+        kda.kda_commit(layer, cu, s["pool"], si, s["recs"][par], nacc, pending=s["pending"],
+                       stream=st)
+        if ev is not None:
+            ev[2].record(st)
+
+    K = args.steps
+    c = 0
+    for _ in range(max(args.warmup, 2 * nsets)):   # every set has pending counts
+        dstep(c, stream)
+        c += 1
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        dstep(c, stream, ev[i])
+        c += 1
+    torch.cuda.synchronize()
+    tv = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    tc = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    # one graph per (set, record parity); the replay order keeps each set's
+    # parity alternating, as the eager loop did
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for j in range(2 * nsets):
+            dstep(c + j, side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    c += 2 * nsets
+    graphs = {}
+    for j in range(2 * nsets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dstep(c + j, torch.cuda.current_stream())
+        graphs[(c + j) % (2 * nsets)] = g
+    for _ in range(args.warmup):
+        graphs[c % (2 * nsets)].replay()
+        c += 1
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        graphs[c % (2 * nsets)].replay()
+        c += 1
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    zeros = np.zeros(B, np.uint8)
+    _, vdef, _ = deferred_bytes(T, n_commit, zeros, n_commit, zeros, valid, H)
+    v_ms = float(tv.mean())
+    return {
+        "ms_per_step": ms,
+        "value": tok_verify / (ms * 1e-3),
+        "step_bytes": vdef,
+        "step_gbs": vdef / (ms * 1e6),
+        "kda_verify_deferred": dict(avg_us=v_ms * 1e3, median_us=float(np.median(tv)) * 1e3,
+                                    bytes=vdef, gbs=vdef / (v_ms * 1e6),
+                                    frac_of_peak=vdef / (v_ms * 1e6) / PEAK_HBM_GBS,
+                                    traffic=measured_traffic("kda_verify_deferred", "decode")),
+        "kda_commit_deferring": dict(avg_us=float(tc.mean()) * 1e3,
+                                     median_us=float(np.median(tc)) * 1e3),
+        "note": "kda_verify_deferred folds the previous step's accepted records (each set's "
+                "counts repeat) and stores the checkpoint, then verifies; the commit writes "
+                "only the pending counts",
+    }
 
 
 def device_copy_gbs(torch, stream) -> float:
