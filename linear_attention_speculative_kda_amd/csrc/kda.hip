@@ -374,23 +374,30 @@ template <int MODE, int BV>
 __device__ __forceinline__ void stage_load(Raw<BV>& x, const Params& p, const Ctx& c, bool fold,
                                            int c0, int m) {
   constexpr int VPL = BV / 32;
+  // Branch-free: the half-waves without a token read the head's g_bias row
+  // instead (512 bytes, more than any of the reads below spans) and drop
+  // what they read. A branch around the loads would put a control-flow join
+  // between them and the next loads, where the compiler's register copies
+  // wait for them to arrive.
   x.active = c.hw < m;
-  if (!x.active) return;
   const int j = c0 + c.hw, l32 = c.l32;
-  const uint16_t *k, *g, *v, *b, *q = nullptr;
-  if (fold) {
-    const long long base = ((long long)c.ri * c.H + c.head) * p.Q + j;
-    k = ((MODE == kDeferred) ? p.pk : p.rk) + base * KD;
-    g = ((MODE == kDeferred) ? p.pg : p.rg) + base * KD;
-    v = ((MODE == kDeferred) ? p.pv : p.rv) + base * KD;
-    b = ((MODE == kDeferred) ? p.pb : p.rb) + base;
-  } else {
-    const long long tok = (long long)c.bos + j;
-    k = p.k + tok * p.sk + c.head * KD;
-    g = p.g + tok * p.sg + c.head * KD;
-    v = p.v + tok * p.sv + c.head * KD;
-    b = p.beta + tok * p.sb + c.head;
-    q = p.q + tok * p.sq + c.head * KD;
+  const uint16_t* safe = reinterpret_cast<const uint16_t*>(p.g_bias + c.head * KD);
+  const uint16_t *k = safe, *g = safe, *v = safe, *b = safe, *q = safe;
+  if (x.active) {
+    if (fold) {
+      const long long base = ((long long)c.ri * c.H + c.head) * p.Q + j;
+      k = ((MODE == kDeferred) ? p.pk : p.rk) + base * KD;
+      g = ((MODE == kDeferred) ? p.pg : p.rg) + base * KD;
+      v = ((MODE == kDeferred) ? p.pv : p.rv) + base * KD;
+      b = ((MODE == kDeferred) ? p.pb : p.rb) + base;
+    } else {
+      const long long tok = (long long)c.bos + j;
+      k = p.k + tok * p.sk + c.head * KD;
+      g = p.g + tok * p.sg + c.head * KD;
+      v = p.v + tok * p.sv + c.head * KD;
+      b = p.beta + tok * p.sb + c.head;
+      q = p.q + tok * p.sq + c.head * KD;
+    }
   }
   x.k = *reinterpret_cast<const uint2*>(k + 4 * l32);
   x.g = *reinterpret_cast<const uint2*>(g + 4 * l32);
@@ -398,7 +405,8 @@ __device__ __forceinline__ void stage_load(Raw<BV>& x, const Params& p, const Ct
   x.q = fold ? make_uint2(0, 0) : *reinterpret_cast<const uint2*>(q + 4 * l32);
 #pragma unroll
   for (int e = 0; e < VPL; ++e) x.v[e] = v[c.tile * BV + l32 * VPL + e];
-  x.b = (l32 == 0) ? *b : (uint16_t)0;
+  const uint16_t bv = *b;
+  x.b = (l32 == 0) ? bv : (uint16_t)0;
 }
 
 // Write a staged window token's raw inputs to its record row (the first Q
@@ -749,6 +757,35 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       // the records last: stores issued behind the state loads would make
       // later register reuse wait for those loads
       store_records<BV>(raw, p, c, 0);
+      return;
+    }
+  }
+
+  // Deferred verify of a row with a pending replay (it fits one chunk: the
+  // count is clamped to the record window): the window's token loads go out
+  // with the records' and the tile's, so the verify's inputs are in
+  // registers by the time the folded state has been stored, and no load
+  // issued behind that store waits for its write.
+  if constexpr (MODE == kDeferred) {
+    if (chunk && nfold <= CH) {
+      Raw<BV> rf, rv;
+      stage_load<MODE, BV>(rf, p, c, true, 0, nfold);
+      stage_load<MODE, BV>(rv, p, c, false, 0, nmain);
+      __builtin_amdgcn_sched_barrier(0);
+      float S[R][16];
+      load_tile<R, BV>(S, sbase, c);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_compute<MODE, BV, CH>(st, rf, p, c, true, 0);
+      lds_barrier();
+      seq_tokens<R, BV, CH>(S, st, p, c, nfold, false, 0);
+      store_tile<R, BV>(S, fbase, c);
+      if (nmain > 0) {
+        lds_barrier();   // the fold's staged tokens are consumed
+        stage_compute<MODE, BV, CH>(st, rv, p, c, false, 0, false);
+        lds_barrier();
+        chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos);
+        store_records<BV>(rv, p, c, 0);
+      }
       return;
     }
   }
