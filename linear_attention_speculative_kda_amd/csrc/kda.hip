@@ -30,7 +30,8 @@
 //    resident capacity, instead of one workgroup per (row, head, tile).
 //  * Verify computes its window in chunked form against the checkpoint: 2T
 //    dot products per value row and a T x T triangular recurrence, no state
-//    stepping and no state write.
+//    stepping and no state write (a window longer than one chunk advances
+//    the state in registers from one chunk to the next).
 //  * No MFMA: the work per state element is a handful of FMAs against a state
 //    that is read once and written at most once; the path is bound by HBM
 //    bandwidth (measured: the verify's dot products on the matrix cores ran no
@@ -505,7 +506,7 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
 //   o_t = b_t + sum_{s<=t} N[t][s] u_s
 // which is the per-token loop's math (decay, delta rule, update, output)
 // with 2m dot products per value row instead of 4m passes over it. Windows
-// longer than one chunk run through the per-token loop.
+// longer than one chunk run chunk after chunk (chunk_advance in between).
 //
 // coef_phase: the per-chunk vectors and coefficients, from the staged k^,
 // q^, exp(g), by 256 threads (c.tid 0..255; c.hw and c.l32 relative to them).
@@ -604,26 +605,27 @@ __device__ __forceinline__ void chunk_dots(const float (&S)[R][16], const StageC
 }
 
 // chunk_recur: the T x T triangular recurrence per value row and the
-// outputs (lane p8 of the group stores token p8's output, to o[tok0 + p8]).
+// outputs (lane p8 of the group stores token p8's output, to o[tok0 + p8]);
+// u receives the chunk's u_t.
 template <int R, int BV, int TMAX, int NT>
 __device__ __forceinline__ void chunk_recur(const StageChunk<BV, NT>& st, const Params& p,
                                             const Ctx& c, int T, long long tok0,
-                                            const float (&a)[R][TMAX], const float (&b)[R][TMAX]) {
+                                            const float (&a)[R][TMAX], const float (&b)[R][TMAX],
+                                            float (&u)[R][TMAX]) {
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     const int vloc = row_in_tile(rr, c);
-    float u[TMAX];
     float mine = 0.0f;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
         float x = st.vt[t][vloc] - a[rr][t];
 #pragma unroll
-        for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[s], x);
-        u[t] = st.bt[t] * x;
+        for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[rr][s], x);
+        u[rr][t] = st.bt[t] * x;
         float y = b[rr][t];
 #pragma unroll
-        for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[s], y);
+        for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[rr][s], y);
         if (c.p8 == t) mine = y;
       }
     }
@@ -632,14 +634,38 @@ __device__ __forceinline__ void chunk_recur(const StageChunk<BV, NT>& st, const 
   }
 }
 
+// chunk_advance: the state after the chunk's T tokens, for a window longer
+// than one chunk: per token the decay and the rank-1 update with the u_t the
+// chunk form found (the per-token step without its dot products).
 template <int R, int BV, int TMAX, int NT>
-__device__ __forceinline__ void chunk_verify(const float (&S)[R][16], StageChunk<BV, NT>& st,
-                                             const Params& p, const Ctx& c, int T, long long tok0) {
+__device__ __forceinline__ void chunk_advance(float (&S)[R][16], const StageChunk<BV, NT>& st,
+                                              const Ctx& c, int T, const float (&u)[R][TMAX]) {
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    if (t < T) {
+      float kh[16], dk[16];
+      lds_row16(st.kh[t], c.p8, kh);
+      lds_row16(st.dk[t], c.p8, dk);
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S[rr][e] = fmaf(kh[e], u[rr][t], S[rr][e] * dk[e]);
+    }
+  }
+}
+
+// One chunk of T <= TMAX window tokens; with `more`, S is advanced past them
+// for the next chunk.
+template <int R, int BV, int TMAX, int NT>
+__device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, NT>& st,
+                                             const Params& p, const Ctx& c, int T, long long tok0,
+                                             bool more = false) {
   coef_phase<BV, TMAX, NT>(st, c, T);
   lds_barrier();
-  float a[R][TMAX], b[R][TMAX];
+  float a[R][TMAX], b[R][TMAX], u[R][TMAX];
   chunk_dots<R, BV, TMAX, NT>(S, st, c, T, a, b);
-  chunk_recur<R, BV, TMAX, NT>(st, p, c, T, tok0, a, b);
+  chunk_recur<R, BV, TMAX, NT>(st, p, c, T, tok0, a, b, u);
+  if (more) chunk_advance<R, BV, TMAX, NT>(S, st, c, T, u);
 }
 
 // ------------------------------------------------------------------ kernel --
@@ -797,8 +823,10 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   const bool first_fold = nfold > 0;
   // align mode: the replay stops at blen for the boundary store
   const int seg0 = (bbase != nullptr) ? blen : nfold;
+  // window tokens per pass: one chunk (TMAX) in the chunked modes
+  constexpr int WCH = kChunk ? TMAX : CH;
   stage_load<MODE, BV>(raw, p, c, first_fold, 0, first_fold ? (seg0 < CH ? seg0 : CH)
-                                                             : (nmain < CH ? nmain : CH));
+                                                             : (nmain < WCH ? nmain : WCH));
   __builtin_amdgcn_sched_barrier(0);
   float S[R][16];
   load_tile<R, BV>(S, sbase, c);
@@ -818,19 +846,31 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       if (bbase != nullptr && c0 == blen) store_tile<R, BV>(S, bbase, c);
     }
     store_tile<R, BV>(S, fbase, c);
-    if (nmain > 0) stage_load<MODE, BV>(raw, p, c, false, 0, nmain < CH ? nmain : CH);
+    if (nmain > 0) stage_load<MODE, BV>(raw, p, c, false, 0, nmain < WCH ? nmain : WCH);
   }
 
   // ---- window: outputs (recurrent, verify, deferred verify) ---------------
   if (nmain > 0) {
     if constexpr (kChunk) {
-      if (chunk) {
+      // chunks of TMAX tokens in chunked form, the state advanced in
+      // registers between them (no per-token loop with outputs here: its
+      // registers would set the whole kernel's allocation)
+      for (int c0 = 0; c0 < nmain; c0 += TMAX) {
+        const int m = (nmain - c0) < TMAX ? (nmain - c0) : TMAX;
+        // the lane indices pass through an empty asm statement once per
+        // chunk, so the compiler derives the chunk's LDS and global
+        // addresses inside the loop instead of keeping them all live
+        // across it
+        Ctx cl = c;
+        asm volatile("" : "+v"(cl.p8), "+v"(cl.grp), "+v"(cl.hw), "+v"(cl.l32), "+v"(cl.tid),
+                     "+v"(cl.wave));
+        if (c0 > 0) stage_load<MODE, BV>(raw, p, cl, false, c0, m);
         lds_barrier();
-        stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0);
+        stage_compute<MODE, BV, CH>(st, raw, p, cl, false, c0);
         lds_barrier();
-        chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos);
-        return;
+        chunk_verify<R, BV, TMAX, CH>(S, st, p, cl, m, (long long)bos + c0, c0 + m < nmain);
       }
+      return;
     }
     for (int c0 = 0; c0 < nmain; c0 += CH) {
       const int m = (nmain - c0) < CH ? (nmain - c0) : CH;
