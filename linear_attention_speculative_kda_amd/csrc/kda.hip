@@ -40,7 +40,8 @@
 //    or reassociated by the compiler.
 //  * Every index read from device memory (cu_seqlens, slots, record rows,
 //    accepted and pending counts, block tables) is range-checked before use.
-// The conv-state compaction of the commit is a separate small copy kernel.
+// The conv-state compaction of the commit is a separate small copy kernel
+// (16-byte spans through LDS for the dense in-place layout).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1017,6 +1018,8 @@ struct ConvParams {
   const int* slots;
   const int* num_accepted;
   int num_rows, conv_dim, history, window;
+  int width;          // token columns per channel
+  int chans;          // in-place kernel: channels per workgroup (a multiple of 8)
   AlignRef align;
 };
 struct ConvTable {
@@ -1074,6 +1077,50 @@ __global__ __launch_bounds__(kConvThreads) void conv_compact_kernel(ConvParams p
       for (int j = 0; j < HIST; ++j) fout[off + (long long)j * L.token_stride] = fv[u][j];
     }
   }
+}
+
+// The in-place compaction (no block table) of a dense [blocks, channels,
+// width] layout: the channel rows of a span are one contiguous run of
+// bytes, and every 128-byte line of it is read and written anyway (a row
+// is a few columns). A workgroup moves `chans` channels of one (row, layer):
+// 16-byte loads of the whole span into LDS, the kept columns moved to the
+// front of each row there (one thread per channel, all of its reads before
+// its writes), 16-byte stores of the span back. The columns from HIST on
+// are written back as they were read.
+constexpr int kConvSpanBytes = 32768;
+
+template <int HIST>
+__global__ __launch_bounds__(kConvThreads) void conv_compact_span_kernel(ConvParams p, ConvTable t) {
+  __shared__ uint4 buf[kConvSpanBytes / 16];
+  const int row = blockIdx.y;
+  const ConvRef& L = t.l[blockIdx.z];
+  const int src = p.slots[row];
+  if (src <= 0 || src >= L.num_blocks) return;
+  const int bos = p.cu[row], eos = p.cu[row + 1];
+  int T = eos - bos;
+  if (bos < 0 || T < 0) T = 0;
+  int n = p.num_accepted[row];
+  n = n < 0 ? 0 : n;
+  n = n < T ? n : T;
+  n = n < p.window ? n : p.window;
+  if (n == 0) return;
+  const int w = p.width;
+  const int c0 = blockIdx.x * p.chans;
+  const int nch = (p.conv_dim - c0) < p.chans ? (p.conv_dim - c0) : p.chans;
+  uint4* span = reinterpret_cast<uint4*>(L.state + (long long)src * L.block_stride + (long long)c0 * w);
+  const int nvec = nch * w / 8;   // the host keeps spans whole 16-byte units
+  for (int i = threadIdx.x; i < nvec; i += kConvThreads) buf[i] = span[i];
+  __syncthreads();
+  uint16_t* b16 = reinterpret_cast<uint16_t*>(buf);
+  for (int ch = threadIdx.x; ch < nch; ch += kConvThreads) {
+    uint16_t v[HIST];
+#pragma unroll
+    for (int j = 0; j < HIST; ++j) v[j] = b16[ch * w + n - 1 + j];
+#pragma unroll
+    for (int j = 0; j < HIST; ++j) b16[ch * w + j] = v[j];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nvec; i += kConvThreads) span[i] = buf[i];
 }
 
 // ------------------------------------------------------------------- host --
@@ -1682,6 +1729,7 @@ kda_status kda_conv_compact(const kda_conv_state* layers, int32_t num_layers, in
   p.conv_dim = conv_dim;
   p.history = history;
   p.window = window;
+  p.width = width;
   p.align = align_ref(align);
   ConvTable t{};
   for (int l = 0; l < num_layers; ++l) {
@@ -1692,6 +1740,35 @@ kda_status kda_conv_compact(const kda_conv_state* layers, int32_t num_layers, in
     t.l[l].num_blocks = layers[l].num_blocks;
   }
   void* args[] = {&p, &t};
+  // in place on dense rows, whole 16-byte units: the span kernel
+  bool span = align == nullptr && (long long)conv_dim * width % 8 == 0;
+  for (int l = 0; l < num_layers && span; ++l) {
+    const kda_conv_state& c = layers[l];
+    span = c.token_stride == 1 && c.dim_stride == width && c.block_stride % 8 == 0 &&
+           c.block_stride >= (long long)conv_dim * width && aligned(c.state, 16);
+  }
+  if (span) {
+    int chans = (kConvSpanBytes / 2 / width) & ~7;
+    chans = chans < 1024 ? chans : 1024;
+    if (chans >= 8) {
+      p.chans = chans;
+      const void* f = nullptr;
+      switch (history) {
+        case 1: f = reinterpret_cast<const void*>(&conv_compact_span_kernel<1>); break;
+        case 2: f = reinterpret_cast<const void*>(&conv_compact_span_kernel<2>); break;
+        case 3: f = reinterpret_cast<const void*>(&conv_compact_span_kernel<3>); break;
+        case 4: f = reinterpret_cast<const void*>(&conv_compact_span_kernel<4>); break;
+        case 5: f = reinterpret_cast<const void*>(&conv_compact_span_kernel<5>); break;
+        case 6: f = reinterpret_cast<const void*>(&conv_compact_span_kernel<6>); break;
+        case 7: f = reinterpret_cast<const void*>(&conv_compact_span_kernel<7>); break;
+        default: f = reinterpret_cast<const void*>(&conv_compact_span_kernel<8>); break;
+      }
+      const dim3 grid((unsigned)((conv_dim + chans - 1) / chans), (unsigned)num_rows,
+                      (unsigned)num_layers);
+      const hipError_t e = hipLaunchKernel(f, grid, dim3(kConvThreads), args, 0, stream);
+      return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    }
+  }
   const void* fn = nullptr;
   switch (history) {
     case 1: fn = reinterpret_cast<const void*>(&conv_compact_kernel<1>); break;

@@ -151,3 +151,32 @@ def test_conv_compact_against_oracle(aligned):
         ref.conv_compact(want, cu, int(cu[-1]), nacc, src, Q, hist, al_np)
         got = devs[l].cpu().numpy().view(np.uint16)
         assert np.array_equal(got, want), f"layer {l}: {np.argwhere(got != want)[:5].tolist()}"
+
+
+@pytest.mark.parametrize("dim,hist,Q", [(300, 3, 4), (2500, 3, 4), (2056, 4, 8), (301, 3, 4),
+                                        (4096, 1, 4)])
+def test_conv_compact_dense_layers(dim, hist, Q):
+    """Every layer in the dense [blocks, channels, width] layout, in place:
+    the span kernel when channels x width is a whole number of 16-byte
+    units (one or several spans per row, a short last span), else the
+    per-channel kernel; bitwise against the oracle either way."""
+    B, layers = 24, 2
+    width = Q + hist - 1
+    say(f"conv compaction dense layers: dim={dim} hist={hist} Q={Q} width={width}")
+    rng = np.random.default_rng(dim + hist)
+    blocks = B + 3
+    src = rng.permutation(np.arange(1, B + 1)).astype(np.int32)
+    src[[2, 7]] = [0, -1]
+    T = rng.integers(0, Q + 1, size=B)
+    cu = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    nacc = rng.integers(-1, Q + 2, size=B).astype(np.int32)
+    states0 = [rng.integers(0, 1 << 16, size=(blocks, dim, width), dtype=np.uint16)
+               for _ in range(layers)]
+    devs = [to_dev(c.view(np.int16)) for c in states0]
+    kda.kda_conv_compact(devs, to_dev(cu), to_dev(src), to_dev(nacc), Q, hist)
+    torch.cuda.synchronize()
+    for l in range(layers):
+        want = states0[l].copy()
+        ref.conv_compact(want, cu, int(cu[-1]), nacc, src, Q, hist)
+        got = devs[l].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), f"layer {l}: {np.argwhere(got != want)[:5].tolist()}"
