@@ -78,7 +78,7 @@ def kernel_key(name: str) -> str:
             return call
     if "kda_commit_list" in name:
         return "kda_commit_deferring"     # a commit with pending counts, by row list
-    if "conv_compact_kernel" in name:
+    if "conv_compact" in name:
         return "kda_conv_compact"
     return name
 
