@@ -32,10 +32,11 @@
 //    dot products per value row and a T x T triangular recurrence, no state
 //    stepping and no state write (a window longer than one chunk advances
 //    the state in registers from one chunk to the next).
-//  * No MFMA: the work per state element is a handful of FMAs against a state
-//    that is read once and written at most once; the path is bound by HBM
-//    bandwidth (measured: the verify's dot products on the matrix cores ran no
-//    faster).
+//  * Matrix cores only for the verify of 8-token chunks, where the 16 dot
+//    products per value row bound the vector lanes (fp32 MFMA). Elsewhere the
+//    work per state element is a handful of FMAs against a state read once
+//    and written at most once: bound by HBM bandwidth, and the matrix cores
+//    ran no faster there (measured).
 //  * -ffp-contract=off: every FMA is an explicit fmaf, nothing is contracted
 //    or reassociated by the compiler.
 //  * Every index read from device memory (cu_seqlens, slots, record rows,
@@ -669,6 +670,122 @@ __device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, N
   if (more) chunk_advance<R, BV, TMAX, NT>(S, st, c, T, u);
 }
 
+// ------------------------------------------------- matrix-core chunk verify --
+//
+// With 8-token chunks the 2T = 16 dot products per value row dominate the
+// verify's vector-ALU time. They form a small matrix product D = A B, A the
+// 16 decayed vectors (Gamma_t k^_t, Gamma_t q^_t; rows of unused tokens
+// read as zero) over the key channels and B the state tile (key channel x
+// value row), which v_mfma_f32_16x16x4_f32 computes in fp32 (fp32 products,
+// fp32 accumulation). Each wave owns 16-row blocks of the tile, RB of them.
+//
+// Operand layout for lane l, i = l % 16, g = l / 16: A[i][g] and B[g][i]
+// are one register each; register r of D holds D[4g + r][i]. The state is
+// loaded straight into the B layout: lane l holds value row i of its block
+// and, for chunk c = 0..7, the key channels 16c + 4g + e (e = 0..3) with one
+// 16-byte load; component e feeds the chunk's e-th instruction, and A is
+// read from LDS with the same channel mapping (only the order of the terms
+// of each sum differs from the vector form). Row i of A is vector
+// t = 4 (i / 8) + i % 4: Gamma_t k^_t for i % 8 < 4, Gamma_t q^_t otherwise;
+// so D register r of lane group g holds a_t (g even) or b_t (g odd) for
+// t = 4 (g / 2) + r. The recurrence then runs in lanes 0..15, one value row
+// each, after the a_t, b_t of the row are gathered there with lane-row
+// swaps.
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Value row of the tile held by (block blk, wave, lane).
+__device__ __forceinline__ int mfma_row(int blk, int wave, int lane) {
+  return blk * (NWAVES * 16) + wave * 16 + (lane & 15);
+}
+
+template <int RB>
+__device__ __forceinline__ void load_tile_mfma(float4 (&S)[RB][8], const float* tile_base,
+                                               int wave, int lane) {
+  const int ch = 4 * (lane >> 4);
+#pragma unroll
+  for (int blk = 0; blk < RB; ++blk) {
+    const float* src = tile_base + mfma_row(blk, wave, lane) * KD + ch;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) S[blk][c] = *reinterpret_cast<const float4*>(src + 16 * c);
+  }
+}
+
+// D for each block; two accumulators per block (even and odd chunks) keep
+// two independent chains in flight.
+template <int RB, int BV, int NT>
+__device__ __forceinline__ void mfma_dots(const float4 (&S)[RB][8], const StageChunk<BV, NT>& st,
+                                          int T, int lane, floatx4 (&D)[RB]) {
+  const int i = lane & 15, g = lane >> 4;
+  const int t = 4 * (i >> 3) + (i & 3);
+  const bool live = t < T;
+  const float* vec = (((i >> 2) & 1) ? st.ga[live ? t : 0] : st.al[live ? t : 0]) + 4 * g;
+  floatx4 acc[RB][2];
+#pragma unroll
+  for (int blk = 0; blk < RB; ++blk) {
+    acc[blk][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+    acc[blk][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float4 a = *reinterpret_cast<const float4*>(vec + 16 * c);
+    if (!live) a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int blk = 0; blk < RB; ++blk) {
+      floatx4& d = acc[blk][c & 1];
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, S[blk][c].x, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, S[blk][c].y, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, S[blk][c].z, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, S[blk][c].w, d, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int blk = 0; blk < RB; ++blk) D[blk] = acc[blk][0] + acc[blk][1];
+}
+
+// The value of lane (l % 16) + 16 * from, for lanes 0..15 (v_permlane16_swap
+// and v_permlane32_swap exchange 16-lane rows of a register).
+__device__ __forceinline__ float from_row(float v, int from) {
+  uint32_t x = __float_as_uint(v);
+  if (from & 2) x = __builtin_amdgcn_permlane32_swap(x, x, false, false)[1];
+  if (from & 1) x = __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
+  return __uint_as_float(x);
+}
+
+// Gather a_t and b_t into lanes 0..15, then the triangular recurrence and
+// the outputs of the lane's value row (lanes 0..15 store).
+template <int RB, int BV, int TMAX, int NT>
+__device__ __forceinline__ void mfma_recur(const floatx4 (&D)[RB], const StageChunk<BV, NT>& st,
+                                           const Params& p, const Ctx& c, int lane, int T,
+                                           long long tok0) {
+#pragma unroll
+  for (int blk = 0; blk < RB; ++blk) {
+    float a[TMAX], b[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const int r = t & 3, half = t >> 2;
+      a[t] = from_row(D[blk][r], 2 * half);
+      b[t] = from_row(D[blk][r], 2 * half + 1);
+    }
+    const int vloc = mfma_row(blk, c.wave, lane);
+    uint16_t* orow = p.o + (tok0 * c.H + c.head) * KD + c.tile * BV + vloc;
+    float u[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        float x = st.vt[t][vloc] - a[t];
+#pragma unroll
+        for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[s], x);
+        u[t] = st.bt[t] * x;
+        float y = b[t];
+#pragma unroll
+        for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[s], y);
+        if (lane < 16) orow[(long long)t * c.H * KD] = f32_to_bf16(y);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ kernel --
 
 // One workgroup's work: (row, head, tile) from its logical block index b.
@@ -770,6 +887,27 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   // their first use lets the compiler copy the state registers there, which
   // waits for the whole tile before the token staging can start.
   // (kda_verify_deferred takes it too for rows with nothing to fold.)
+  if constexpr (MODE == kVerify && TMAX == CH && R >= 2) {
+    if (chunk) {   // 8-token chunks: the dot products on the matrix cores
+      constexpr int RB = R / 2;
+      const int lane = c.tid & 63;
+      Raw<BV> raw;
+      stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
+      __builtin_amdgcn_sched_barrier(0);
+      float4 S[RB][8];
+      load_tile_mfma<RB>(S, sbase + c.tile * BV * KD, c.wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0, false);
+      lds_barrier();
+      coef_phase<BV, TMAX, CH>(st, c, nmain);
+      lds_barrier();
+      floatx4 D[RB];
+      mfma_dots<RB, BV, CH>(S, st, nmain, lane, D);
+      mfma_recur<RB, BV, TMAX, CH>(D, st, p, c, lane, nmain, (long long)bos);
+      store_records<BV>(raw, p, c, 0);
+      return;
+    }
+  }
   if constexpr (MODE == kVerify || MODE == kDeferred) {
     if (chunk && nfold == 0) {
       Raw<BV> raw;
