@@ -688,9 +688,8 @@ __device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, N
 // of each sum differs from the vector form). Row i of A is vector
 // t = 4 (i / 8) + i % 4: Gamma_t k^_t for i % 8 < 4, Gamma_t q^_t otherwise;
 // so D register r of lane group g holds a_t (g even) or b_t (g odd) for
-// t = 4 (g / 2) + r. The recurrence then runs in lanes 0..15, one value row
-// each, after the a_t, b_t of the row are gathered there with lane-row
-// swaps.
+// t = 4 (g / 2) + r. The recurrence then runs one value row per lane, after
+// the a_t, b_t of each row are regrouped through LDS.
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -743,45 +742,46 @@ __device__ __forceinline__ void mfma_dots(const float4 (&S)[RB][8], const StageC
   for (int blk = 0; blk < RB; ++blk) D[blk] = acc[blk][0] + acc[blk][1];
 }
 
-// The value of lane (l % 16) + 16 * from, for lanes 0..15 (v_permlane16_swap
-// and v_permlane32_swap exchange 16-lane rows of a register).
-__device__ __forceinline__ float from_row(float v, int from) {
-  uint32_t x = __float_as_uint(v);
-  if (from & 2) x = __builtin_amdgcn_permlane32_swap(x, x, false, false)[1];
-  if (from & 1) x = __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
-  return __uint_as_float(x);
-}
-
-// Gather a_t and b_t into lanes 0..15, then the triangular recurrence and
-// the outputs of the lane's value row (lanes 0..15 store).
+// The triangular recurrence and the outputs, one value row per lane: the
+// wave's D registers go to LDS (row-major, a_0..a_7 then b_0..b_7 per value
+// row), and lane l < 16 RB takes row mfma_row(l / 16, wave, l), one of the
+// rows this wave computed, so only the wave's own LDS writes are read.
 template <int RB, int BV, int TMAX, int NT>
-__device__ __forceinline__ void mfma_recur(const floatx4 (&D)[RB], const StageChunk<BV, NT>& st,
-                                           const Params& p, const Ctx& c, int lane, int T,
-                                           long long tok0) {
+__device__ __forceinline__ void mfma_recur_rows(const floatx4 (&D)[RB], const StageChunk<BV, NT>& st,
+                                                float (*dx)[17], const Params& p, const Ctx& c,
+                                                int lane, int T, long long tok0) {
+  const int g = lane >> 4;
+  const int col = (g & 1) * 8 + 4 * (g >> 1);
 #pragma unroll
   for (int blk = 0; blk < RB; ++blk) {
-    float a[TMAX], b[TMAX];
+    float* d = dx[mfma_row(blk, c.wave, lane)] + col;
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      const int r = t & 3, half = t >> 2;
-      a[t] = from_row(D[blk][r], 2 * half);
-      b[t] = from_row(D[blk][r], 2 * half + 1);
-    }
-    const int vloc = mfma_row(blk, c.wave, lane);
-    uint16_t* orow = p.o + (tok0 * c.H + c.head) * KD + c.tile * BV + vloc;
-    float u[TMAX];
+    for (int r = 0; r < 4; ++r) d[r] = D[blk][r];
+  }
+  // LDS operations of one wave complete in order; the reads below see the
+  // writes above (wait for them anyway before the reads)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane >= 16 * RB) return;
+  const int vloc = mfma_row(lane >> 4, c.wave, lane);
+  const float* row = dx[vloc];
+  float a[TMAX], b[TMAX], u[TMAX];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (t < T) {
-        float x = st.vt[t][vloc] - a[t];
+  for (int t = 0; t < TMAX; ++t) {
+    a[t] = row[t];
+    b[t] = row[8 + t];
+  }
+  uint16_t* orow = p.o + (tok0 * c.H + c.head) * KD + c.tile * BV + vloc;
 #pragma unroll
-        for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[s], x);
-        u[t] = st.bt[t] * x;
-        float y = b[t];
+  for (int t = 0; t < TMAX; ++t) {
+    if (t < T) {
+      float x = st.vt[t][vloc] - a[t];
 #pragma unroll
-        for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[s], y);
-        if (lane < 16) orow[(long long)t * c.H * KD] = f32_to_bf16(y);
-      }
+      for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[s], x);
+      u[t] = st.bt[t] * x;
+      float y = b[t];
+#pragma unroll
+      for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[s], y);
+      orow[(long long)t * c.H * KD] = f32_to_bf16(y);
     }
   }
 }
@@ -903,7 +903,8 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       lds_barrier();
       floatx4 D[RB];
       mfma_dots<RB, BV, CH>(S, st, nmain, lane, D);
-      mfma_recur<RB, BV, TMAX, CH>(D, st, p, c, lane, nmain, (long long)bos);
+      __shared__ float dx[BV][17];
+      mfma_recur_rows<RB, BV, TMAX, CH>(D, st, dx, p, c, lane, nmain, (long long)bos);
       store_records<BV>(raw, p, c, 0);
       return;
     }
