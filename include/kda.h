@@ -234,7 +234,9 @@ kda_status kda_verify_deferred(const kda_layer* layer, const kda_tokens* tokens,
  *   cu_seqlens, num_rows, record_rows, num_accepted, pending, eager: shared,
  *   with the meaning of kda_commit; each layer does exactly what kda_commit
  *   would do for it (same bits). pending (deferred mode) holds one count per
- *   record row for all layers and is written once.
+ *   record row for all layers and is written once, as the first layer's pool
+ *   sees the row (a slot at or beyond that pool's num_slots counts as
+ *   skipped there).
  *   align (host struct, may be NULL): the align mode above, which writes
  *   the final (and boundary) block instead of the source; only without
  *   pending (deferred mode with align -> KDA_ERR_UNSUPPORTED).
