@@ -148,3 +148,44 @@ def test_deferred_row_list_capacity(B):
     say(f"case deferred row list B={B} H=1 layers=2 steps=3")
     res = gpu_flows(run)
     compare(run, *res, sample=[(1, [0, B - 1])])
+
+
+@pytest.mark.parametrize("B,H", [(32, 16), (128, 32)])
+def test_deferred_eight_token_windows(B, H):
+    """Record window and windows of 8 tokens, with 512 and 4096 (row, head)
+    pairs (64- and 128-row tiles). The deferred flow's folded states equal
+    the eager flow's commits bit for bit (one replay code); its outputs
+    match the eager flow's within the output tolerance: kda_verify takes
+    its 8-token dot products on the matrix cores, kda_verify_deferred (after
+    its fold) on the vector lanes, so the sums run in different orders."""
+    from workloads import make_batch
+    from .helpers import dev_layer
+    batch = make_batch("deep", B=B, H=H)
+    B, H, Q = batch.num_rows, batch.H, batch.Q
+    assert Q == 8 and np.all(batch.seq_lens() == 8)
+    say(f"case deferred 8-token windows B={B} H={H}")
+    L = dev_layer(batch)
+    toks = DevTokens(batch.tokens)
+    cu, si = to_dev(batch.cu_seqlens), to_dev(batch.state_indices)
+    nacc = to_dev(batch.num_accepted.astype(np.int32))
+    pool0 = to_dev(batch.initial_pool())
+    pool_e, pool_d = pool0.clone(), pool0.clone()
+    ntok = batch.tokens.num_tokens
+    rec_e = dev_records(B, H, Q)
+    rec_d = [dev_records(B, H, Q), dev_records(B, H, Q)]
+    pending = torch.zeros(B, dtype=torch.int32, device=DEV)
+    outs = []
+    for step in range(3):
+        oe = torch.empty((ntok, H, 128), dtype=torch.bfloat16, device=DEV)
+        od = torch.empty_like(oe)
+        kda.kda_verify(L, *toks.args(), cu, pool_e, si, rec_e, oe)
+        kda.kda_verify_deferred(L, *toks.args(), cu, pool_d, si, rec_d[(step + 1) % 2], pending,
+                                rec_d[step % 2], od)
+        kda.kda_commit(L, cu, pool_e, si, rec_e, nacc)
+        kda.kda_commit(L, cu, pool_d, si, rec_d[step % 2], nacc, pending=pending)
+        outs.append((oe, od))
+    kda.kda_flush(L, pool_d, si, rec_d[2 % 2], pending, rec_d[(2 + 1) % 2])
+    torch.cuda.synchronize()
+    for step, (oe, od) in enumerate(outs):
+        check_o(bits_host(od), bits_host(oe), what=f"deferred o vs eager o, step {step}")
+    assert torch.equal(pool_e.view(torch.int32), pool_d.view(torch.int32)), "pools differ"
