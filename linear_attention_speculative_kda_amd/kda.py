@@ -1,5 +1,7 @@
-"""Python front end of libkda: the four calls of include/kda.h, taking torch
-tensors that live on the GPU. Marshalling only; the computation is in HIP.
+"""Python front end of libkda: the calls of include/kda.h (recurrent, verify,
+commit, deferred verify and flush, the multi-layer commit and flush, the
+conv-state compaction), taking torch tensors that live on the GPU.
+Marshalling only; the computation is in HIP.
 
 Tensor conventions (K = V = 128):
   q, k, v, g      [num_tokens, H, K] bf16 (or any 2-byte dtype holding bf16
