@@ -179,8 +179,9 @@ def main():
         print(json.dumps(out, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this path shards by requests and heads with "
-              "no exchange, and no multi-GPU run is part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU only: the path shards by requests and heads with no "
+              "exchange between GPUs, so a multi-GPU figure is N independent one-GPU runs.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
