@@ -180,3 +180,34 @@ def test_conv_compact_dense_layers(dim, hist, Q):
         ref.conv_compact(want, cu, int(cu[-1]), nacc, src, Q, hist)
         got = devs[l].cpu().numpy().view(np.uint16)
         assert np.array_equal(got, want), f"layer {l}: {np.argwhere(got != want)[:5].tolist()}"
+
+
+def test_conv_compact_padded_blocks():
+    """Dense rows inside blocks with padding between them (the block stride
+    longer than channels x width) and a misaligned start: the span kernel
+    for the first, the per-channel kernel for the second; the padding and
+    everything outside the moved columns keep their bits."""
+    B, dim, hist, Q = 12, 1024, 3, 4
+    width = Q + hist - 1
+    rng = np.random.default_rng(23)
+    blocks = B + 2
+    src = rng.permutation(np.arange(1, B + 1)).astype(np.int32)
+    T = rng.integers(0, Q + 1, size=B)
+    cu = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    nacc = rng.integers(-1, Q + 2, size=B).astype(np.int32)
+    for pad, offset in ((8, 0), (8, 1)):
+        say(f"conv compaction padded blocks: pad={pad} offset={offset}")
+        stride = dim * width + pad
+        flat0 = rng.integers(0, 1 << 16, size=blocks * stride + offset, dtype=np.uint16)
+        flat = to_dev(flat0.view(np.int16))
+        view = torch.as_strided(flat, (blocks, dim, width), (stride, width, 1), offset)
+        kda.kda_conv_compact([view], to_dev(cu), to_dev(src), to_dev(nacc), Q, hist)
+        torch.cuda.synchronize()
+        want_flat = flat0.copy()
+        want = np.lib.stride_tricks.as_strided(want_flat[offset:], (blocks, dim, width),
+                                               (stride * 2, width * 2, 2))
+        tmp = np.ascontiguousarray(want)
+        ref.conv_compact(tmp, cu, int(cu[-1]), nacc, src, Q, hist)
+        want[...] = tmp
+        got = flat.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want_flat), f"pad={pad} offset={offset}: {np.argwhere(got != want_flat)[:5].tolist()}"
