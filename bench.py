@@ -1,20 +1,24 @@
 """Benchmark: KDA speculative verify + commit on one MI355X.
 
-A step is one pass of the whole path over one batch: kda_verify (window from
-the checkpoints, outputs and records) followed by kda_commit (accepted prefix
-replayed into the checkpoints). The default workload is the decode batch:
-B=64 requests, H=32 heads, K=V=128, T=4 tokens each (1 + 3 draft), bf16
-activations, fp32 checkpoints made by 64 random prefill tokens through the
-library's own recurrence, num_accepted ~ Binomial(4, 0.7).
+A step is one decode step of the whole path in serving order over several
+layers: every layer's kda_verify (window from the checkpoints, outputs and
+records), then every layer's commit (accepted prefix replayed into the
+checkpoints) in one kda_commit_layers launch, as the commit runs once per
+step for all layers after sampling. Each layer has its own pool, inputs and
+records (12 layers by default). The default workload is the decode batch per
+layer: B=64 requests, H=32 heads, K=V=128, T=4 tokens each (1 + 3 draft),
+bf16 activations, fp32 checkpoints made by 64 random prefill tokens through
+the library's own recurrence, num_accepted ~ Binomial(4, 0.7).
 
-Inputs are resident in HBM before the timed region. To keep the 256 MB
-Infinity Cache (MALL) from serving the checkpoints, the steps rotate over
-several independent copies of the inputs (pools, activations, records), so
-consecutive steps touch different memory.
+Inputs are resident in HBM before the timed region. The layers' checkpoints
+(12 x 128 MiB) exceed the 256 MB Infinity Cache (MALL) many times over: at
+most the last two layers' checkpoints can still be there when the commit
+reads them, and nothing of one step is left for the next.
 
-Printed: one JSON line (metric, value = step tokens/s, per-kernel times,
-achieved HBM bandwidth against the 8 TB/s peak, and the CPU oracle's rate on a
-bounded sample of the same workload).
+Printed: one JSON line (metric, value = verified tokens/s per layer call,
+per-kernel times, achieved HBM bandwidth against the 8 TB/s peak, the same
+step in the deferred flow, and the CPU oracle's rate on a bounded sample of
+the same workload).
 """
 
 from __future__ import annotations
@@ -153,7 +157,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "deep", "ragged", "deferred"])
-    ap.add_argument("--sets", type=int, default=6, help="independent input copies rotated")
+    ap.add_argument("--sets", type=int, default=12,
+                    help="layers per step, each with its own pool, inputs and records")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -162,7 +167,7 @@ def parse():
                     help="commit in align mode: a block table sends each row's state to other "
                          "blocks of the pool (decode/deep/ragged workloads)")
     ap.add_argument("--per-layer-commit", action="store_true",
-                    help="deferred workload: one kda_commit per layer instead of kda_commit_layers")
+                    help="one kda_commit per layer instead of one kda_commit_layers per step")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="merge two rocprofv3 --pmc runs of --workload into profiles/traffic.json "
                          "and exit")
@@ -224,7 +229,7 @@ def main():
         torch.cuda.synchronize()
         del qkv, o_pre
 
-    # ---- independent input sets (defeat the MALL between steps)
+    # ---- one input set per layer: pool, activations, records, outputs
     sets = []
     for _ in range(args.sets):
         qkv = up_bf16(batch.tokens.qkv)
@@ -239,9 +244,19 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def verify(s):
+    # Each input set stands for one layer of the model: a step is the
+    # serving order of one decode step, every layer's kda_verify (the forward
+    # pass), then every layer's commit in one kda_commit_layers launch (after
+    # sampling). With 12 sets the step touches 12 x 128 MiB of checkpoints:
+    # the 256 MB MALL can carry at most the last two layers' checkpoints
+    # from their verify to the commit.
+    L = len(sets)
+    pools = [s["pool"] for s in sets]
+    recs = [s["rec"] for s in sets]
+
+    def verify(s, st):
         kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
-                       s["rec"], s["o"], stream=stream)
+                       s["rec"], s["o"], stream=st)
 
     align = None
     if args.align:
@@ -254,39 +269,49 @@ def main():
         bt = np.array(free[:2 * B], np.int32).reshape(B, 2)
         align = kda.Align(up(bt), up(np.full(B, 2, np.int32)), 4)
 
-    def commit(s, st=None):
-        st = stream if st is None else st
+    def commit_one(s, st):
         if align is None:
             kda.kda_commit(layer, cu, s["pool"], si, s["rec"], nacc, stream=st)
         else:
             kda.kda_commit_layers([layer], cu, [s["pool"]], si, [s["rec"]], nacc, align=align,
                                   stream=st)
 
-    for i in range(args.warmup):
-        s = sets[i % len(sets)]
-        verify(s)
-        commit(s)
+    def commit_all(st):
+        if args.per_layer_commit:
+            for s in sets:
+                commit_one(s, st)
+        else:
+            kda.kda_commit_layers([layer] * L, cu, pools, si, recs, nacc, align=align, stream=st)
+
+    def step(st, ev=None):
+        for i, s in enumerate(sets):
+            if ev is not None:
+                ev[i].record(st)
+            verify(s, st)
+        if ev is not None:
+            ev[L].record(st)
+        commit_all(st)
+        if ev is not None:
+            ev[L + 1].record(st)
+
+    for _ in range(max(1, args.warmup // L)):
+        step(stream)
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, events around every launch on the launch stream
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 2)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
-        s = sets[i % len(sets)]
-        ev[i][0].record(stream)
-        verify(s)
-        ev[i][1].record(stream)
-        commit(s)
-        ev[i][2].record(stream)
+        step(stream, ev[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    tv = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    tc = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    tv = np.array([e[i].elapsed_time(e[i + 1]) for e in ev for i in range(L)])
+    tc = np.array([e[L].elapsed_time(e[L + 1]) for e in ev])
 
     n_commit = np.minimum(np.maximum(batch.num_accepted, 0), np.minimum(T, Q))
     vbytes, cbytes = algorithmic_bytes(T, n_commit, valid, H)
@@ -297,69 +322,82 @@ def main():
     tok_commit = int(n_commit[valid].sum())
     ms_step = total_ms / K
     v_ms, c_ms = float(tv.mean()), float(tc.mean())
+    commit_launches = L if args.per_layer_commit else 1
+    commit_name = "kda_commit" if args.per_layer_commit and align is None else "kda_commit_layers"
+    c_launch_bytes = cbytes * L / commit_launches
+    c_launch_ms = c_ms / commit_launches
     kernels = {
-        "kda_verify": dict(avg_us=v_ms * 1e3, median_us=float(np.median(tv)) * 1e3,
-                           bytes=vbytes, gbs=vbytes / (v_ms * 1e6),
-                           tokens_per_s=tok_verify / (v_ms * 1e-3)),
-        "kda_commit": dict(avg_us=c_ms * 1e3, median_us=float(np.median(tc)) * 1e3,
-                           bytes=cbytes, gbs=cbytes / (c_ms * 1e6),
-                           tokens_per_s=tok_commit / (c_ms * 1e-3)),
+        "kda_verify": dict(launches_per_step=L, avg_us=v_ms * 1e3,
+                           median_us=float(np.median(tv)) * 1e3, bytes=vbytes,
+                           gbs=vbytes / (v_ms * 1e6), tokens_per_s=tok_verify / (v_ms * 1e-3)),
+        commit_name: dict(launches_per_step=commit_launches, layers_per_launch=L // commit_launches,
+                          avg_us=c_launch_ms * 1e3, median_us=float(np.median(tc)) / commit_launches * 1e3,
+                          bytes=c_launch_bytes, gbs=c_launch_bytes / (c_launch_ms * 1e6),
+                          tokens_per_s=tok_commit * L / (c_ms * 1e-3)),
     }
     for kinfo in kernels.values():
         kinfo["frac_of_peak"] = kinfo["gbs"] / PEAK_HBM_GBS
-    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    # the dominant kernel: the one that takes the larger share of the step
+    dom = "kda_verify" if L * v_ms >= c_ms else commit_name
 
-    # ---- context: kda_verify without a commit before it. In the step, the
-    # previous commit's 128 MiB of new state is still being written back from
-    # the MALL while the next verify streams its checkpoints, so the verify's
-    # event time carries part of the commit's writes.
-    ev_iso = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    for i in range(len(sets)):
-        verify(sets[i])
-    torch.cuda.synchronize()
-    for i in range(K):
-        s = sets[i % len(sets)]
-        ev_iso[i][0].record(stream)
-        verify(s)
-        ev_iso[i][1].record(stream)
-    torch.cuda.synchronize()
-    ti = np.array([a.elapsed_time(b) for a, b in ev_iso])
-    verify_isolated = dict(avg_us=float(ti.mean()) * 1e3, median_us=float(np.median(ti)) * 1e3,
-                           gbs=vbytes / (float(ti.mean()) * 1e6))
-    verify_isolated["frac_of_peak"] = verify_isolated["gbs"] / PEAK_HBM_GBS
-
-    # ---- the step as a serving loop runs it: captured in a HIP graph (one
-    # graph per input set: verify then commit), replayed for exactly K steps.
+    # ---- the step as a serving loop runs it: captured in one HIP graph
+    # (every layer's verify, then the commit), replayed for exactly K steps.
     # The eager loop above gives the per-kernel times; this one the step.
-    graphs = []
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        for s in sets:
-            kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
-                           s["rec"], s["o"], stream=side)
-            commit(s, side)
+        step(side)
     stream.wait_stream(side)
     torch.cuda.synchronize()
-    for s in sets:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cap = torch.cuda.current_stream()
-            kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
-                           s["rec"], s["o"], stream=cap)
-            commit(s, cap)
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream())
+    for _ in range(max(1, args.warmup // L)):
+        graph.replay()
     torch.cuda.synchronize()
     g_start = torch.cuda.Event(enable_timing=True)
     g_end = torch.cuda.Event(enable_timing=True)
     g_start.record(stream)
     for i in range(K):
-        graphs[i % len(graphs)].replay()
+        graph.replay()
     g_end.record(stream)
     torch.cuda.synchronize()
     ms_step_graph = g_start.elapsed_time(g_end) / K
+    ms_layer = ms_step_graph / L
+
+    # ---- context: one layer's verify then its own commit, back to back
+    # (kda_commit per layer). The commit then re-reads the checkpoints the
+    # verify has just read, partly from the MALL, and the next verify streams
+    # its checkpoints while that commit's new state is written back to HBM.
+    Ki = max(4, min(K, 60))
+    evi = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(Ki)]
+    for i in range(L):
+        verify(sets[i], stream)
+        commit_one(sets[i], stream)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for i in range(Ki):
+        s = sets[i % L]
+        evi[i][0].record(stream)
+        verify(s, stream)
+        evi[i][1].record(stream)
+        commit_one(s, stream)
+        evi[i][2].record(stream)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    ti_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evi]))
+    ti_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evi]))
+    ms_inter = a0.elapsed_time(a1) / Ki
+    interleaved = {
+        "ms_per_layer_step": ms_inter,
+        "value": tok_verify / (ms_inter * 1e-3),
+        "kda_verify_avg_us": ti_v * 1e3,
+        "kda_commit_avg_us": ti_c * 1e3,
+        "gbs": (vbytes + cbytes) / (ms_inter * 1e6),
+        "note": "each layer's verify followed at once by its own single-layer commit (eager "
+                "launches); not the serving order",
+    }
 
     deferred = None if align is not None else decode_deferred_flow(
         args, torch, kda, layer, sets, cu, si, nacc, stream, T, n_commit, valid, H, B, Q, dev,
@@ -367,9 +405,10 @@ def main():
 
     copy_gbs = device_copy_gbs(torch, stream)
 
+    step_bytes = L * (vbytes + cbytes)
     result = {
         "metric": "KDA verify+commit tokens/s and achieved HBM GB/s vs peak (B=64,H=32,T=4)",
-        "value": tok_verify / (ms_step_graph * 1e-3),
+        "value": L * tok_verify / (ms_step_graph * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -382,12 +421,14 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{batch.name}: B={B} H={H} K=V=128 T={'ragged' if batch.name == 'ragged' else int(T.max())} "
-                        f"Q={Q}, bf16 activations, fp32 checkpoints, one layer call per kernel",
-            "B": B, "H": H, "K": 128, "V": 128, "T": int(T.max()), "window": Q,
-            "verified_tokens_per_step": tok_verify, "committed_tokens_per_step": tok_commit,
+                        f"Q={Q}, bf16 activations, fp32 checkpoints; a step = {L} layers (own pool, "
+                        f"inputs and records each): every layer's kda_verify, then "
+                        f"{'one kda_commit per layer' if args.per_layer_commit else 'one kda_commit_layers for all layers'}; "
+                        f"value = verified tokens per second per layer call",
+            "B": B, "H": H, "K": 128, "V": 128, "T": int(T.max()), "window": Q, "layers_per_step": L,
+            "verified_tokens_per_layer": tok_verify, "committed_tokens_per_layer": tok_commit,
             "commit": "align mode (block table, destinations other than the sources)" if args.align
                       else "in place",
-            "input_sets_rotated": len(sets),
         },
         "roofline": {
             "bound": "hbm",
@@ -399,15 +440,16 @@ def main():
             "traffic": measured_traffic(dom, args.workload),
         },
         "kernels": kernels,
-        "kda_verify_without_preceding_commit": verify_isolated,
-        "step_gbs": (vbytes + cbytes) / (ms_step_graph * 1e6),
-        "step_frac_of_peak": (vbytes + cbytes) / (ms_step_graph * 1e6) / PEAK_HBM_GBS,
-        "step_timing": "HIP graph replay (verify + commit per step); per-kernel times from "
-                       "HIP events around eager launches",
+        "ms_per_layer_step": ms_layer,
+        "step_gbs": step_bytes / (ms_step_graph * 1e6),
+        "step_frac_of_peak": step_bytes / (ms_step_graph * 1e6) / PEAK_HBM_GBS,
+        "step_timing": "HIP graph replay of whole steps; per-kernel times from HIP events around "
+                       "eager launches",
         "ms_per_step_eager": ms_step,
-        "value_eager": tok_verify / (ms_step * 1e-3),
-        "commit_tokens_per_s": tok_commit / (c_ms * 1e-3),
+        "value_eager": L * tok_verify / (ms_step * 1e-3),
+        "commit_tokens_per_s": tok_commit * L / (c_ms * 1e-3),
         "verify_tokens_per_s": tok_verify / (v_ms * 1e-3),
+        "interleaved": interleaved,
         "copy_gbs_measured": copy_gbs,
     }
     if deferred is not None:
@@ -421,69 +463,77 @@ def main():
 
 def decode_deferred_flow(args, torch, kda, layer, sets, cu, si, nacc, stream, T, n_commit, valid,
                          H, B, Q, dev, tok_verify):
-    """The same step in the deferred flow: kda_verify_deferred folds the
-    records the previous step of the same input set accepted into the
-    checkpoint (and stores it) while it verifies; the commit then only
-    records this step's accepted counts as pending (no eager rows). Two
-    record buffers per set alternate. Timed like the eager step: events
-    around eager launches for the kernels, HIP graphs for the step."""
+    """The same step in the deferred flow, in the same serving order: every
+    layer's kda_verify_deferred (each folds the records its layer accepted
+    in the previous step into the checkpoint, stores it and verifies), then
+    one commit for all layers that only records this step's accepted counts
+    as pending (no eager rows; the counts are per request, shared by the
+    layers). Two record buffers per layer alternate. Timed like the eager
+    step: events around eager launches for the kernels, HIP graphs for the
+    step."""
+    L = len(sets)
     for s in sets:
         s["recs"] = [s["rec"], kda.allocate_records(B, H, Q, dev)]
-        s["pending"] = torch.zeros(B, dtype=torch.int32, device=dev)
-    nsets = len(sets)
+    pools = [s["pool"] for s in sets]
+    rec_by_parity = [[s["recs"][par] for s in sets] for par in range(2)]
+    pending = torch.zeros(B, dtype=torch.int32, device=dev)
 
     def dstep(c, st, ev=None):
-        s = sets[c % nsets]
-        par = (c // nsets) % 2
+        par = c % 2
+        for i, s in enumerate(sets):
+            if ev is not None:
+                ev[i].record(st)
+            kda.kda_verify_deferred(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"],
+                                    si, s["recs"][1 - par], pending, s["recs"][par], s["o"], stream=st)
         if ev is not None:
-            ev[0].record(st)
-        kda.kda_verify_deferred(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
-                                s["recs"][1 - par], s["pending"], s["recs"][par], s["o"], stream=st)
+            ev[L].record(st)
+        if args.per_layer_commit:
+            for s in sets:
+                kda.kda_commit(layer, cu, s["pool"], si, s["recs"][par], nacc, pending=pending,
+                               stream=st)
+        else:
+            kda.kda_commit_layers([layer] * L, cu, pools, si, rec_by_parity[par], nacc,
+                                  pending=pending, stream=st)
         if ev is not None:
-            ev[1].record(st)
-        kda.kda_commit(layer, cu, s["pool"], si, s["recs"][par], nacc, pending=s["pending"],
-                       stream=st)
-        if ev is not None:
-            ev[2].record(st)
+            ev[L + 1].record(st)
 
     K = args.steps
     c = 0
-    for _ in range(max(args.warmup, 2 * nsets)):   # every set has pending counts
+    for _ in range(max(2, args.warmup // L)):   # every layer has pending counts
         dstep(c, stream)
         c += 1
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 2)] for _ in range(K)]
     for i in range(K):
         dstep(c, stream, ev[i])
         c += 1
     torch.cuda.synchronize()
-    tv = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    tc = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    tv = np.array([e[i].elapsed_time(e[i + 1]) for e in ev for i in range(L)])
+    tc = np.array([e[L].elapsed_time(e[L + 1]) for e in ev])
 
-    # one graph per (set, record parity); the replay order keeps each set's
-    # parity alternating, as the eager loop did
+    # one graph per record parity, replayed alternately as the eager loop ran
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        for j in range(2 * nsets):
+        for j in range(2):
             dstep(c + j, side)
     stream.wait_stream(side)
     torch.cuda.synchronize()
-    c += 2 * nsets
+    c += 2
     graphs = {}
-    for j in range(2 * nsets):
+    for j in range(2):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             dstep(c + j, torch.cuda.current_stream())
-        graphs[(c + j) % (2 * nsets)] = g
-    for _ in range(args.warmup):
-        graphs[c % (2 * nsets)].replay()
+        graphs[(c + j) % 2] = g
+    for _ in range(max(2, args.warmup // L)):
+        graphs[c % 2].replay()
         c += 1
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(K):
-        graphs[c % (2 * nsets)].replay()
+        graphs[c % 2].replay()
         c += 1
     b.record(stream)
     torch.cuda.synchronize()
@@ -493,18 +543,20 @@ def decode_deferred_flow(args, torch, kda, layer, sets, cu, si, nacc, stream, T,
     v_ms = float(tv.mean())
     return {
         "ms_per_step": ms,
-        "value": tok_verify / (ms * 1e-3),
-        "step_bytes": vdef,
-        "step_gbs": vdef / (ms * 1e6),
+        "ms_per_layer_step": ms / L,
+        "value": L * tok_verify / (ms * 1e-3),
+        "layer_step_bytes": vdef,
+        "step_gbs": L * vdef / (ms * 1e6),
         "kda_verify_deferred": dict(avg_us=v_ms * 1e3, median_us=float(np.median(tv)) * 1e3,
                                     bytes=vdef, gbs=vdef / (v_ms * 1e6),
                                     frac_of_peak=vdef / (v_ms * 1e6) / PEAK_HBM_GBS,
                                     traffic=measured_traffic("kda_verify_deferred", "decode")),
-        "kda_commit_deferring": dict(avg_us=float(tc.mean()) * 1e3,
+        "kda_commit_deferring": dict(launches_per_step=L if args.per_layer_commit else 1,
+                                     avg_us=float(tc.mean()) * 1e3,
                                      median_us=float(np.median(tc)) * 1e3),
-        "note": "kda_verify_deferred folds the previous step's accepted records (each set's "
-                "counts repeat) and stores the checkpoint, then verifies; the commit writes "
-                "only the pending counts",
+        "note": "every layer's kda_verify_deferred folds the records its layer accepted in the "
+                "previous step (the counts repeat) and stores the checkpoint, then verifies; the "
+                "commit then writes only the pending counts",
     }
 
 

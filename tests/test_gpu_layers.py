@@ -121,3 +121,40 @@ def test_flush_layers_matches_per_layer():
         for i, s in enumerate(run.state_indices):
             changed = not np.array_equal(before[s], after[s])
             assert changed == (pend[run.record_rows[i]] > 0), f"layer {l} row {i}"
+
+
+@pytest.mark.parametrize("name,layers", [("decode", 12), ("deep", 4), ("ragged", 4)])
+def test_commit_layers_full_size(name, layers):
+    """The benchmark's commit launch: every layer of a full-size workload in
+    one kda_commit_layers call gives, layer by layer, the bits of kda_commit
+    (itself bit-exact with kda_recurrent over the accepted prefix at these
+    sizes). Each layer has its own checkpoints (seeded N(0, 0.02) on the
+    device) and the records of its own verify."""
+    from workloads import make_batch
+    from .helpers import dev_layer
+    batch = make_batch(name)
+    B, H, Q = batch.num_rows, batch.H, batch.Q
+    say(f"commit_layers full size: {name} B={B} H={H} layers={layers}")
+    lay = dev_layer(batch)
+    toks = DevTokens(batch.tokens)
+    cu, si, nacc = to_dev(batch.cu_seqlens), to_dev(batch.state_indices), to_dev(batch.num_accepted)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4242)
+    o = torch.empty((batch.tokens.num_tokens, H, 128), dtype=torch.bfloat16, device=DEV)
+    one, many, recs = [], [], []
+    for _ in range(layers):
+        p = torch.empty((batch.num_slots, H, 128, 128), dtype=torch.float32, device=DEV)
+        p.normal_(0.0, 0.02, generator=gen)
+        rec = dev_records(B, H, Q)
+        kda.kda_verify(lay, *toks.args(), cu, p, si, rec, o)
+        one.append(p)
+        many.append(p.clone())
+        recs.append(rec)
+    for l in range(layers):
+        kda.kda_commit(lay, cu, one[l], si, recs[l], nacc)
+    kda.kda_commit_layers([lay] * layers, cu, many, si, recs, nacc)
+    torch.cuda.synchronize()
+    for l in range(layers):
+        assert torch.equal(bits(one[l]), bits(many[l])), f"{name}: layer {l}"
+    del one, many, recs
+    torch.cuda.empty_cache()
