@@ -254,9 +254,12 @@ def main():
     pools = [s["pool"] for s in sets]
     recs = [s["rec"] for s in sets]
 
+    # the window bound a serving batch knows on the host (1 + num_spec)
+    max_seqlen = int(T.max())
+
     def verify(s, st):
         kda.kda_verify(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["pool"], si,
-                       s["rec"], s["o"], stream=st)
+                       s["rec"], s["o"], stream=st, max_seqlen=max_seqlen)
 
     align = None
     if args.align:
@@ -426,6 +429,7 @@ def main():
                         f"{'one kda_commit per layer' if args.per_layer_commit else 'one kda_commit_layers for all layers'}; "
                         f"value = verified tokens per second per layer call",
             "B": B, "H": H, "K": 128, "V": 128, "T": int(T.max()), "window": Q, "layers_per_step": L,
+            "max_seqlen": max_seqlen,
             "verified_tokens_per_layer": tok_verify, "committed_tokens_per_layer": tok_commit,
             "commit": "align mode (block table, destinations other than the sources)" if args.align
                       else "in place",
@@ -651,7 +655,7 @@ def deferred_leg(args, torch, kda, dev):
     def eager_step(s, ev=None):
         for l in range(L):
             kda.kda_verify(layers[l], *toks[l][:5], cu, pools[l], si, recs[l][0], o,
-                           record_rows=rr, stream=stream)
+                           record_rows=rr, stream=stream, max_seqlen=T)
         if args.per_layer_commit:
             for l in range(L):
                 kda.kda_commit(layers[l], cu, pools[l], si, recs[l][0], nacc[s % S],

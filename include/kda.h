@@ -94,6 +94,15 @@ typedef struct kda_tokens {
   const int32_t* cu_seqlens;  /* [num_rows + 1] int32 */
   int32_t num_rows;
   int32_t num_tokens;       /* rows of the token arrays (and of o) */
+  /* An upper bound on every row's window T_i that the caller guarantees, or
+   * 0 when unknown (pages: kda.py, _forward, where the speculative window's
+   * maximum query length num_spec + 1 is known on the host and handed to the
+   * short convolution). Used by kda_verify only: with 1 <= max_seqlen <= 8 it
+   * runs kernels built for windows of at most that many tokens, and a row
+   * longer than max_seqlen is then skipped like a row without a slot
+   * (nothing of it is written). Larger values run the general kernels.
+   * Negative -> KDA_ERR_SHAPE (every call). */
+  int32_t max_seqlen;
 } kda_tokens;
 
 /* The checkpoint pool of one layer (host struct of device pointers). */
@@ -168,7 +177,8 @@ kda_status kda_recurrent(const kda_layer* layer, const kda_tokens* tokens,
  * raw k, v, g, beta of tokens 0..min(T_i, Q)-1 to record row r, where
  * r = record_rows[i] (record_rows == NULL: r = i, which needs
  * num_rows <= rec->rows, else KDA_ERR_CAPACITY). The pool is read only: no
- * state is written.
+ * state is written. With tokens->max_seqlen in 1..8 the rows longer than it
+ * are skipped (see kda_tokens); the others give the same bits as without it.
  * Errors as kda_recurrent, plus: records overlapping o, the pool or the
  * token arrays -> KDA_ERR_ALIAS; misaligned records -> KDA_ERR_ALIGN.
  */

@@ -44,6 +44,7 @@ class KdaTokens(ctypes.Structure):
         ("cu_seqlens", c_ptr),
         ("num_rows", ctypes.c_int32),
         ("num_tokens", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
     ]
 
 

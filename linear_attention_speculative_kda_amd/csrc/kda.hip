@@ -123,6 +123,7 @@ struct Params {
   const int* cu;
   int num_rows;
   int num_tokens;
+  int guess_len;           // short verify: predicted uniform window length, 0: none
   // pool
   float* state;
   long long slot_stride;
@@ -808,7 +809,10 @@ __device__ __forceinline__ bool commit_now(const Params& p, int row) {
   return p.pending == nullptr || (p.eager != nullptr && p.eager[row] != 0);
 }
 
-template <int MODE, int R, int TMAX>
+// SHORT (verify only): a kernel for windows of at most TMAX tokens, the
+// caller's bound; it has no code for longer windows, whose registers would
+// set the allocation of the whole kernel, and it skips longer rows.
+template <int MODE, int R, int TMAX, bool SHORT = false>
 __device__ __forceinline__ void kda_block(const Params& p, int b) {
   constexpr int BV = R * NWAVES * 8;   // value rows per workgroup
   constexpr bool kChunk = (MODE == kVerify || MODE == kDeferred);
@@ -828,6 +832,19 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   c.head = rh % p.H;
   const int row = rh / p.H;
   c.H = p.H;
+
+  // Short verify of uniform windows (the usual speculative batch: every row
+  // has the same 1 + num_spec tokens, row i from token i * len): the window's
+  // token loads go out at the predicted span before the row metadata
+  // arrives. The prediction is checked against cu_seqlens before any use;
+  // a row that does not match loads its tokens again.
+  Raw<BV> raw;
+  const int gl = (SHORT && TMAX == 4) ? p.guess_len : 0;
+  if (gl > 0) {
+    Ctx cs = c;
+    cs.bos = row * gl;
+    stage_load<MODE, BV>(raw, p, cs, false, 0, gl);
+  }
 
   // ---- row prologue: span, slot, record row, counts -----------------------
   const bool flush = MODE == kDeferred && p.flush;
@@ -891,7 +908,6 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
     if (chunk) {   // 8-token chunks: the dot products on the matrix cores
       constexpr int RB = R / 2;
       const int lane = c.tid & 63;
-      Raw<BV> raw;
       stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
       __builtin_amdgcn_sched_barrier(0);
       float4 S[RB][8];
@@ -911,8 +927,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   }
   if constexpr (MODE == kVerify || MODE == kDeferred) {
     if (chunk && nfold == 0) {
-      Raw<BV> raw;
-      stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
+      if (!(gl > 0 && bos == row * gl && nmain == gl)) stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
       __builtin_amdgcn_sched_barrier(0);
       float S[R][16];
       load_tile<R, BV>(S, sbase, c);
@@ -925,6 +940,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       store_records<BV>(raw, p, c, 0);
       return;
     }
+    if constexpr (SHORT) return;   // a window longer than the caller's bound
   }
 
   // Deferred verify of a row with a pending replay (it fits one chunk: the
@@ -959,7 +975,6 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   // The first chunk's token loads go out before the state tile's: loads
   // complete in issue order, so the staging math then waits for its own
   // inputs only while the 64 KiB tile is still in flight.
-  Raw<BV> raw;
   const bool first_fold = nfold > 0;
   // align mode: the replay stops at blen for the boundary store
   const int seg0 = (bbase != nullptr) ? blen : nfold;
@@ -1032,9 +1047,9 @@ __device__ __forceinline__ int logical_block(int nb) {
   return (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
 }
 
-template <int MODE, int R, int TMAX>
+template <int MODE, int R, int TMAX, bool SHORT = false>
 __global__ __launch_bounds__(NTHREADS) void kda_kernel(Params p) {
-  kda_block<MODE, R, TMAX>(p, logical_block(p.total_blocks));
+  kda_block<MODE, R, TMAX, SHORT>(p, logical_block(p.total_blocks));
 }
 
 // The same work for several layers in one grid: logical block b belongs to
@@ -1302,7 +1317,7 @@ kda_status check_pool(const kda_pool* P, int H, int num_rows) {
 
 kda_status check_tokens(const kda_tokens* t, int H) {
   if (!t || !t->cu_seqlens) return KDA_ERR_NULL;
-  if (t->num_rows < 0 || t->num_tokens < 0) return KDA_ERR_SHAPE;
+  if (t->num_rows < 0 || t->num_tokens < 0 || t->max_seqlen < 0) return KDA_ERR_SHAPE;
   // With no tokens every row is empty and no token array is read.
   if (t->num_rows == 0 || t->num_tokens == 0) return KDA_OK;
   if (!t->q || !t->k || !t->v || !t->g || !t->beta) return KDA_ERR_NULL;
@@ -1423,28 +1438,28 @@ int tile_rows_for(int mode, long long pairs) {
   return pairs >= 512 ? 64 : 32;
 }
 
-template <int MODE, int R, int TMAX>
+template <int MODE, int R, int TMAX, bool SHORT = false>
 kda_status launch_r(Params& p, hipStream_t stream) {
   p.tiles = KD / (32 * R);
   const long long blocks = (long long)p.num_rows * p.H * p.tiles;
   if (blocks > 0x7FFFFFFFLL) return KDA_ERR_SHAPE;
   p.total_blocks = (int)blocks;
   void* args[] = {&p};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel<MODE, R, TMAX>),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel<MODE, R, TMAX, SHORT>),
                                        dim3((unsigned)blocks), dim3(NTHREADS), args, 0, stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 // The verify modes keep 2 * R * TMAX dot products in registers: windows of
 // up to 4 tokens get a kernel with TMAX = 4 (fewer registers, more waves);
-// longer windows TMAX = 8 (CH). Longer rows still run, through the per-token
-// loop.
-template <int MODE, int TMAX>
+// longer windows TMAX = 8 (CH). Rows longer than TMAX still run, chunk after
+// chunk, except in the short kernels.
+template <int MODE, int TMAX, bool SHORT = false>
 kda_status launch_t(Params& p, hipStream_t stream) {
   switch (tile_rows_for(MODE, (long long)p.num_rows * p.H)) {
-    case 32: return launch_r<MODE, 1, TMAX>(p, stream);
-    case 64: return launch_r<MODE, 2, TMAX>(p, stream);
-    default: return launch_r<MODE, 4, TMAX>(p, stream);
+    case 32: return launch_r<MODE, 1, TMAX, SHORT>(p, stream);
+    case 64: return launch_r<MODE, 2, TMAX, SHORT>(p, stream);
+    default: return launch_r<MODE, 4, TMAX, SHORT>(p, stream);
   }
 }
 
@@ -1551,6 +1566,17 @@ template <int MODE>
 kda_status launch(Params& p, hipStream_t stream) {
   if ((MODE == kVerify || MODE == kDeferred) && p.Q <= 4) return launch_t<MODE, 4>(p, stream);
   return launch_t<MODE, CH>(p, stream);
+}
+
+// kda_verify with the caller's bound on every window (1..CH tokens): the
+// short kernels, TMAX = 4 for bounds up to 4. When the token count is a
+// whole multiple of the row count within the bound, the rows are predicted
+// to be uniform windows of that length (checked per row in the kernel).
+kda_status launch_verify_short(Params& p, int max_seqlen, hipStream_t stream) {
+  const int g = p.num_tokens % p.num_rows == 0 ? p.num_tokens / p.num_rows : 0;
+  p.guess_len = (g >= 1 && g <= max_seqlen) ? g : 0;
+  if (max_seqlen <= 4) return launch_t<kVerify, 4, true>(p, stream);
+  return launch_t<kVerify, CH, true>(p, stream);
 }
 
 }  // namespace
@@ -1695,6 +1721,8 @@ kda_status kda_verify(const kda_layer* layer, const kda_tokens* tokens, const kd
   set_records(p, rec);
   p.record_rows = record_rows;
   p.o = o;
+  if (tokens->max_seqlen >= 1 && tokens->max_seqlen <= CH)
+    return launch_verify_short(p, tokens->max_seqlen, stream);
   return launch<kVerify>(p, stream);
 }
 

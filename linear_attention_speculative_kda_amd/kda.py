@@ -103,7 +103,7 @@ def _act(t: torch.Tensor, name: str, H: int) -> int:
     return t.stride(0)
 
 
-def _tokens(q, k, v, g, beta, cu_seqlens, H: int) -> _lib.KdaTokens:
+def _tokens(q, k, v, g, beta, cu_seqlens, H: int, max_seqlen: int | None = None) -> _lib.KdaTokens:
     n = q.shape[0]
     for t, name in ((k, "k"), (v, "v"), (g, "g")):
         if t.shape[0] != n:
@@ -115,7 +115,8 @@ def _tokens(q, k, v, g, beta, cu_seqlens, H: int) -> _lib.KdaTokens:
         q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), g=g.data_ptr(), beta=beta.data_ptr(),
         stride_q=_act(q, "q", H), stride_k=_act(k, "k", H), stride_v=_act(v, "v", H),
         stride_g=_act(g, "g", H), stride_beta=beta.stride(0) if n > 0 else H,
-        cu_seqlens=cu_seqlens.data_ptr(), num_rows=cu_seqlens.numel() - 1, num_tokens=n)
+        cu_seqlens=cu_seqlens.data_ptr(), num_rows=cu_seqlens.numel() - 1, num_tokens=n,
+        max_seqlen=0 if max_seqlen is None else int(max_seqlen))
 
 
 def _pool(pool: torch.Tensor, state_indices: torch.Tensor, H: int, rows: int | None = None) -> _lib.KdaPool:
@@ -182,12 +183,15 @@ def kda_recurrent(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indice
 
 
 def kda_verify(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indices,
-               rec: Records, o, record_rows=None, stream=None) -> None:
-    """Verify from the checkpoints: o and raw records; the pool is read only."""
+               rec: Records, o, record_rows=None, stream=None, max_seqlen: int | None = None) -> None:
+    """Verify from the checkpoints: o and raw records; the pool is read only.
+    ``max_seqlen``: an upper bound on every row's window that the caller
+    guarantees (None: unknown); with 1..8 the short kernels run and rows
+    longer than it are skipped."""
     _on_gpu(pool, layer, q, k, v, g, beta, cu_seqlens, state_indices, rec, o, record_rows)
     lib = _lib.load()
     H = layer.num_heads
-    L, T, P = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H), _pool(pool, state_indices, H, cu_seqlens.numel() - 1)
+    L, T, P = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H, max_seqlen), _pool(pool, state_indices, H, cu_seqlens.numel() - 1)
     R = rec.c_struct()
     st = lib.kda_verify(ctypes.byref(L), ctypes.byref(T), ctypes.byref(P), ctypes.byref(R),
                         _opt_ptr(record_rows, torch.int32, "record_rows", cu_seqlens.numel() - 1),

@@ -109,6 +109,7 @@ def test_verify_rejects_bad_tokens():
     assert verify(T=tokens(stride_g=H * K + 2)) == E["KDA_ERR_ALIGN"]     # not a multiple of 4
     assert verify(T=tokens(k=A + 0x100000 + 2 * H * K + 2)) == E["KDA_ERR_ALIGN"]
     assert verify(T=tokens(num_rows=-1)) == E["KDA_ERR_SHAPE"]
+    assert verify(T=tokens(max_seqlen=-1)) == E["KDA_ERR_SHAPE"]
 
 
 def test_verify_rejects_bad_pool_and_records():
@@ -301,3 +302,39 @@ def test_conv_compact_validation():
     assert conv(al=align(width=0)) == E["KDA_ERR_SHAPE"]
     assert conv(n_rows=70000) == E["KDA_ERR_SHAPE"]
     assert conv(n_rows=0) == E["KDA_OK"]
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every host struct of include/kda.h has the size and field offsets the
+    ctypes binding assumes (compiled with the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"kda_layer": _lib.KdaLayer, "kda_tokens": _lib.KdaTokens, "kda_pool": _lib.KdaPool,
+               "kda_records": _lib.KdaRecords, "kda_align": _lib.KdaAlign,
+               "kda_conv_state": _lib.KdaConvState}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "kda.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([cc, "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+                          "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        pytest.skip(f"the header does not compile on the host here: {res.stderr[:200]}")
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        cname, fname, val = line.split()
+        got[(cname, fname)] = int(val)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, f"{cname}.{fname}"
