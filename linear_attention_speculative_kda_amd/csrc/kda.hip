@@ -811,7 +811,9 @@ __device__ __forceinline__ bool commit_now(const Params& p, int row) {
 
 // SHORT (verify only): a kernel for windows of at most TMAX tokens, the
 // caller's bound; it has no code for longer windows, whose registers would
-// set the allocation of the whole kernel, and it skips longer rows.
+// set the allocation of the whole kernel, and it skips longer rows. (The
+// same cut in the deferred verify, 106 -> 96 VGPRs at 64-row tiles, ran 3%
+// slower: the extra resident workgroups contend in its fold and store.)
 template <int MODE, int R, int TMAX, bool SHORT = false>
 __device__ __forceinline__ void kda_block(const Params& p, int b) {
   constexpr int BV = R * NWAVES * 8;   // value rows per workgroup
