@@ -69,8 +69,20 @@ typedef enum kda_status {
   KDA_ERR_ALIGN = 4,        /* pointer or stride not aligned for the vector loads */
   KDA_ERR_ALIAS = 5,        /* an output range overlaps an input or another output */
   KDA_ERR_UNSUPPORTED = 6,  /* head_dim other than 128 */
-  KDA_ERR_LAUNCH = 7        /* the HIP launch reported an error */
+  KDA_ERR_LAUNCH = 7,       /* the HIP launch reported an error */
+  KDA_ERR_METADATA = 8      /* kda_check_rows: a row breaks a precondition (see kda_row_issue) */
 } kda_status;
+
+/* What kda_check_rows found wrong with a row. */
+typedef enum kda_row_issue {
+  KDA_ROW_OK = 0,
+  KDA_ROW_SPAN = 1,          /* cu_seqlens[i] < 0, cu_seqlens[i+1] < cu_seqlens[i] or > num_tokens */
+  KDA_ROW_WINDOW = 2,        /* T_i > max_seqlen (max_seqlen > 0) */
+  KDA_ROW_SLOT_RANGE = 3,    /* state_indices[i] >= num_slots */
+  KDA_ROW_SLOT_DUP = 4,      /* a slot used by an earlier row */
+  KDA_ROW_RECORD_RANGE = 5,  /* record row < -1 or >= rec_rows */
+  KDA_ROW_RECORD_DUP = 6     /* a record row used by an earlier row */
+} kda_row_issue;
 
 /* One layer's gate parameters (host struct). */
 typedef struct kda_layer {
@@ -312,6 +324,27 @@ kda_status kda_conv_compact(const kda_conv_state* layers, int32_t num_layers, in
 
 /* Host: a static, human-readable name for a status code. */
 const char* kda_status_string(kda_status status);
+
+/*
+ * kda_check_rows -- host-side check of the row metadata that the kernels
+ * only range-check (an opt-in debugging aid: the calls above never read
+ * device metadata on the host). Every pointer here is a HOST pointer.
+ * Rows with state_indices[i] <= 0 are skipped rows and pass; for the others:
+ * a well-formed span within num_tokens, T_i <= max_seqlen when max_seqlen > 0
+ * (the window bound of kda_tokens), a slot below num_slots and not shared
+ * with another row (distinct slots, as the pages' one checkpoint per request
+ * requires), and a record row (record_rows[i], or i when record_rows is NULL)
+ * that is -1 (the scratch row: nothing is recorded) or below rec_rows and
+ * not shared with another row. rec_rows < 0 skips the record-row checks.
+ * Returns KDA_OK, or KDA_ERR_METADATA with *bad_row = the first offending row
+ * and *issue = what is wrong with it (both optional); KDA_ERR_NULL for
+ * missing arrays, KDA_ERR_SHAPE for negative sizes. Reads only; allocates
+ * host memory for the duplicate checks (num_slots and rec_rows flags).
+ */
+kda_status kda_check_rows(const int32_t* cu_seqlens, int32_t num_rows, int32_t num_tokens,
+                          const int32_t* state_indices, int32_t num_slots,
+                          const int32_t* record_rows, int32_t rec_rows, int32_t max_seqlen,
+                          int32_t* bad_row, int32_t* issue);
 
 /* Host: the library's build identification (static string). */
 const char* kda_build_info(void);

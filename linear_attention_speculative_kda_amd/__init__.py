@@ -13,6 +13,7 @@ from .kda import (  # noqa: F401
     Records,
     allocate_records,
     MAX_LAYERS,
+    check_rows,
     kda_commit,
     kda_commit_layers,
     kda_conv_compact,

@@ -15,9 +15,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("KDA_LIB", os.path.join(_HERE, "libkda.so"))
 
 KDA_OK = 0
+KDA_ERR_METADATA = 8
 STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_CAPACITY",
     4: "KDA_ERR_ALIGN", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_LAUNCH",
+    8: "KDA_ERR_METADATA",
+}
+ROW_ISSUES = {
+    0: "ok", 1: "malformed span", 2: "window longer than max_seqlen", 3: "slot >= num_slots",
+    4: "slot shared with an earlier row", 5: "record row out of range",
+    6: "record row shared with an earlier row",
 }
 
 c_ptr = ctypes.c_void_p
@@ -122,6 +129,10 @@ def load() -> ctypes.CDLL:
     for fn in ("kda_recurrent", "kda_verify", "kda_commit", "kda_verify_deferred",
                "kda_commit_layers", "kda_flush_layers", "kda_conv_compact"):
         getattr(lib, fn).restype = ctypes.c_int
+    lib.kda_check_rows.argtypes = [c_ptr, ctypes.c_int32, ctypes.c_int32, c_ptr, ctypes.c_int32,
+                                   c_ptr, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_check_rows.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_build_info.argtypes = []

@@ -18,6 +18,7 @@ Tensor conventions (K = V = 128):
 from __future__ import annotations
 
 import ctypes
+import os
 from dataclasses import dataclass
 
 import torch
@@ -170,10 +171,54 @@ def _out(o: torch.Tensor, n: int, H: int) -> int:
     return o.data_ptr()
 
 
+def check_rows(cu_seqlens, state_indices, num_slots: int, num_tokens: int | None = None,
+               record_rows=None, rec_rows: int | None = None, max_seqlen: int | None = None) -> None:
+    """Check on the host the row metadata the kernels only range-check
+    (libkda's kda_check_rows): well-formed spans, windows within max_seqlen,
+    slots below num_slots and distinct, record rows in range and distinct.
+    The int32 tensors may live on any device (they are copied to the host,
+    which synchronises with the GPU). Raises KdaError naming the first bad
+    row."""
+    lib = _lib.load()
+    cu = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    si = state_indices.detach().to("cpu", torch.int32).contiguous()
+    rows = cu.numel() - 1
+    if si.numel() < rows:
+        raise ValueError(f"state_indices has {si.numel()} entries, needs {rows}")
+    rr = None if record_rows is None else record_rows.detach().to("cpu", torch.int32).contiguous()
+    if rr is not None and rr.numel() < rows:
+        raise ValueError(f"record_rows has {rr.numel()} entries, needs {rows}")
+    ntok = int(cu[-1]) if num_tokens is None and rows > 0 else int(num_tokens or 0)
+    bad, what = ctypes.c_int32(-1), ctypes.c_int32(0)
+    st = lib.kda_check_rows(cu.data_ptr(), rows, ntok, si.data_ptr(), int(num_slots),
+                            None if rr is None else rr.data_ptr(),
+                            -1 if rec_rows is None else int(rec_rows),
+                            0 if max_seqlen is None else int(max_seqlen),
+                            ctypes.byref(bad), ctypes.byref(what))
+    if st == _lib.KDA_ERR_METADATA:
+        raise _lib.KdaError("kda_check_rows", st,
+                            f"row {bad.value}: {_lib.ROW_ISSUES.get(what.value, what.value)}")
+    _lib.check("kda_check_rows", st)
+
+
+# KDA_DEBUG_VALIDATE=1: every call below first checks its row metadata on the
+# host (a synchronising copy; for debugging only).
+_DEBUG_VALIDATE = os.environ.get("KDA_DEBUG_VALIDATE", "0") == "1"
+
+
+def _debug_rows(cu_seqlens, state_indices, pool, num_tokens=None, record_rows=None,
+                rec: "Records | None" = None, max_seqlen=None) -> None:
+    if _DEBUG_VALIDATE:
+        check_rows(cu_seqlens, state_indices, pool.shape[0], num_tokens=num_tokens,
+                   record_rows=record_rows, rec_rows=None if rec is None else rec.rows,
+                   max_seqlen=max_seqlen)
+
+
 def kda_recurrent(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indices, o,
                   stream=None) -> None:
     """Plain recurrence: o for every token, final state stored in place."""
     _on_gpu(pool, layer, q, k, v, g, beta, cu_seqlens, state_indices, o)
+    _debug_rows(cu_seqlens, state_indices, pool, q.shape[0])
     lib = _lib.load()
     H = layer.num_heads
     L, T, P = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H), _pool(pool, state_indices, H, cu_seqlens.numel() - 1)
@@ -189,6 +234,7 @@ def kda_verify(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indices,
     guarantees (None: unknown); with 1..8 the short kernels run and rows
     longer than it are skipped."""
     _on_gpu(pool, layer, q, k, v, g, beta, cu_seqlens, state_indices, rec, o, record_rows)
+    _debug_rows(cu_seqlens, state_indices, pool, q.shape[0], record_rows, rec, max_seqlen)
     lib = _lib.load()
     H = layer.num_heads
     L, T, P = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H, max_seqlen), _pool(pool, state_indices, H, cu_seqlens.numel() - 1)
@@ -203,6 +249,7 @@ def kda_commit(layer: Layer, cu_seqlens, pool, state_indices, rec: Records, num_
                record_rows=None, pending=None, eager=None, stream=None) -> None:
     """Commit the accepted prefix (or, with ``pending``, defer it)."""
     _on_gpu(pool, layer, cu_seqlens, state_indices, rec, num_accepted, record_rows, pending, eager)
+    _debug_rows(cu_seqlens, state_indices, pool, None, record_rows, rec)
     lib = _lib.load()
     H = layer.num_heads
     _need(cu_seqlens, torch.int32, "cu_seqlens")
@@ -222,6 +269,7 @@ def kda_verify_deferred(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_
     """Fold the pending replays into the checkpoints, then verify."""
     _on_gpu(pool, layer, q, k, v, g, beta, cu_seqlens, state_indices, rec_prev, pending,
             rec_next, o, record_rows)
+    _debug_rows(cu_seqlens, state_indices, pool, q.shape[0], record_rows, rec_next)
     lib = _lib.load()
     H = layer.num_heads
     L, T, P = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H), _pool(pool, state_indices, H, cu_seqlens.numel() - 1)
@@ -291,6 +339,7 @@ def kda_commit_layers(layers, cu_seqlens, pools, state_indices, recs, num_accept
     instead of the source."""
     _on_gpu(pools[0], cu_seqlens, state_indices, num_accepted, record_rows, pending, eager,
             *layers, *pools, *recs, *(() if align is None else (align.block_table, align.num_computed)))
+    _debug_rows(cu_seqlens, state_indices, pools[0], None, record_rows, recs[0])
     lib = _lib.load()
     _need(cu_seqlens, torch.int32, "cu_seqlens")
     rows = cu_seqlens.numel() - 1

@@ -338,3 +338,68 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(cls), cname
         for fname, _ in cls._fields_:
             assert got[(cname, fname)] == getattr(cls, fname).offset, f"{cname}.{fname}"
+
+
+# -------------------------------------------------- host metadata check --
+
+def check_rows_c(cu, si, num_slots, num_tokens=None, rr=None, rec_rows=-1, max_seqlen=0):
+    """kda_check_rows on host numpy arrays: (status, bad row, issue)."""
+    import numpy as np
+    lib = _lib.load()
+    cu = np.ascontiguousarray(cu, np.int32)
+    si = np.ascontiguousarray(si, np.int32)
+    rr = None if rr is None else np.ascontiguousarray(rr, np.int32)
+    bad, what = ctypes.c_int32(-7), ctypes.c_int32(-7)
+    st = lib.kda_check_rows(cu.ctypes.data, len(cu) - 1, int(cu[-1]) if num_tokens is None else num_tokens,
+                            si.ctypes.data, num_slots, None if rr is None else rr.ctypes.data,
+                            rec_rows, max_seqlen, ctypes.byref(bad), ctypes.byref(what))
+    return st, bad.value, what.value
+
+
+def test_check_rows_accepts_good_metadata():
+    # skipped rows (slot 0 and -1) may have any span and repeat slots
+    cu = [0, 4, 8, 8, 11, 15]
+    si = [3, 1, 0, -1, 2]
+    assert check_rows_c(cu, si, 4, rr=[2, -1, 0, 0, 1], rec_rows=3, max_seqlen=4) == (0, -1, 0)
+    assert check_rows_c(cu, si, 4) == (0, -1, 0)                      # no record check
+    assert check_rows_c([0], [], 4)[0] == 0                           # no rows
+
+
+def test_check_rows_names_the_first_bad_row():
+    M = E["KDA_ERR_METADATA"]
+    # spans
+    assert check_rows_c([0, 4, 3, 8], [1, 2, 3], 4) == (M, 1, 1)      # end before start
+    assert check_rows_c([0, 4, 8, 12], [1, 2, 3], 4, num_tokens=10) == (M, 2, 1)   # beyond the tokens
+    assert check_rows_c([-1, 4, 8], [1, 2], 4) == (M, 0, 1)           # negative start
+    # window longer than the bound
+    assert check_rows_c([0, 4, 9, 12], [1, 2, 3], 4, max_seqlen=4) == (M, 1, 2)
+    # slots
+    assert check_rows_c([0, 1, 2, 3], [1, 4, 2], 4) == (M, 1, 3)      # slot >= num_slots
+    assert check_rows_c([0, 1, 2, 3], [1, 2, 1], 4) == (M, 2, 4)      # shared slot
+    # record rows
+    assert check_rows_c([0, 1, 2, 3], [1, 2, 3], 4, rr=[0, 3, 1], rec_rows=3) == (M, 1, 5)
+    assert check_rows_c([0, 1, 2, 3], [1, 2, 3], 4, rr=[0, -2, 1], rec_rows=3) == (M, 1, 5)
+    assert check_rows_c([0, 1, 2, 3], [1, 2, 3], 4, rr=[0, 1, 0], rec_rows=3) == (M, 2, 6)
+    assert check_rows_c([0, 1, 2, 3], [1, 2, 3], 4, rr=[-1, -1, 1], rec_rows=3) == (0, -1, 0)
+    # identity record rows beyond the record rows
+    assert check_rows_c([0, 1, 2, 3], [1, 2, 3], 4, rec_rows=2) == (M, 2, 5)
+
+
+def test_check_rows_argument_errors():
+    lib = _lib.load()
+    import numpy as np
+    cu = np.zeros(3, np.int32)
+    assert lib.kda_check_rows(None, 2, 0, cu.ctypes.data, 4, None, -1, 0, None, None) == E["KDA_ERR_NULL"]
+    assert lib.kda_check_rows(cu.ctypes.data, -1, 0, cu.ctypes.data, 4, None, -1, 0, None, None) == E["KDA_ERR_SHAPE"]
+    assert lib.kda_check_rows(cu.ctypes.data, 2, 0, cu.ctypes.data, 4, None, -1, -3, None, None) == E["KDA_ERR_SHAPE"]
+
+
+def test_binding_check_rows_raises_with_the_row():
+    import torch
+    import linear_attention_speculative_kda_amd as kda
+    cu = torch.tensor([0, 4, 8, 12], dtype=torch.int32)
+    kda.check_rows(cu, torch.tensor([1, 2, 3], dtype=torch.int32), num_slots=4, max_seqlen=4)
+    with pytest.raises(_lib.KdaError, match="row 2: slot shared"):
+        kda.check_rows(cu, torch.tensor([1, 2, 1], dtype=torch.int32), num_slots=4)
+    with pytest.raises(_lib.KdaError, match="row 0: window longer"):
+        kda.check_rows(cu, torch.tensor([1, 2, 3], dtype=torch.int32), num_slots=4, max_seqlen=3)

@@ -291,3 +291,33 @@ def test_verify_outputs_match_recurrent_outputs(name):
     kda.kda_recurrent(layer, *tok.args(), cu, pool.clone(), si, o_r)
     torch.cuda.synchronize()
     check_o(bits_host(o_v), bits_host(o_r), what=f"{name}: verify o vs recurrent o")
+
+
+def test_debug_validation_checks_rows_before_the_launch(monkeypatch):
+    """With the debug check on (KDA_DEBUG_VALIDATE=1 at import), a call whose
+    rows break a precondition raises before anything is enqueued; good rows
+    run as usual."""
+    import linear_attention_speculative_kda_amd.kda as kda_mod
+    monkeypatch.setattr(kda_mod, "_DEBUG_VALIDATE", True)
+    batch = make_batch("tiny", B=4, H=4)
+    say("case debug validation")
+    L = dev_layer(batch)
+    toks = DevTokens(batch.tokens)
+    pool_np = batch.initial_pool()
+    pool = to_dev(pool_np)
+    cu = to_dev(batch.cu_seqlens)
+    rec = dev_records(4, 4, 4, fill=SENT)
+    o = torch.zeros((16, 4, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(kda.KdaError, match="row 3: slot shared"):
+        kda.kda_verify(L, *toks.args(), cu, pool, to_dev(np.array([1, 2, 3, 1], np.int32)), rec, o)
+    with pytest.raises(kda.KdaError, match="window longer"):
+        kda.kda_verify(L, *toks.args(), cu, pool, to_dev(batch.state_indices), rec, o, max_seqlen=3)
+    with pytest.raises(kda.KdaError, match="record row"):
+        kda.kda_commit(L, cu, pool, to_dev(batch.state_indices), rec, to_dev(batch.num_accepted),
+                       record_rows=to_dev(np.array([0, 1, 1, 2], np.int32)))
+    torch.cuda.synchronize()
+    assert np.all(bits_host(o) == 0), "a rejected call wrote o"
+    assert np.array_equal(pool.cpu().numpy(), pool_np), "a rejected call wrote the pool"
+    kda.kda_verify(L, *toks.args(), cu, pool, to_dev(batch.state_indices), rec, o, max_seqlen=4)
+    kda.kda_commit(L, cu, pool, to_dev(batch.state_indices), rec, to_dev(batch.num_accepted))
+    torch.cuda.synchronize()
