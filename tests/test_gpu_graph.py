@@ -82,3 +82,64 @@ def test_graph_replay_matches_eager(name, B, H):
         # unrelated eager work between replays
         _ = (pool0.sum() + pool_g.abs().max()).item()
     say("  4 replays bitwise equal to eager")
+
+
+def test_graph_replay_of_the_serving_step():
+    """The benchmark's step in one graph: every layer's window-bounded
+    kda_verify (short kernels, predicted spans), then one kda_commit_layers;
+    replays equal the eager step bit for bit."""
+    batch = make_batch("decode", B=16, H=8)
+    rows, H, Q = batch.num_rows, batch.H, batch.Q
+    ntok = batch.tokens.num_tokens
+    L = 3
+    say(f"graph replay of the serving step: decode B={rows} H={H}, {L} layers")
+    layer = dev_layer(batch)
+    tok = DevTokens(batch.tokens)
+    cu, si, nacc = to_dev(batch.cu_seqlens), to_dev(batch.state_indices), to_dev(batch.num_accepted)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    pools0 = []
+    for _ in range(L):
+        p = torch.empty((batch.num_slots, H, 128, 128), dtype=torch.float32, device=DEV)
+        p.normal_(0.0, 0.02, generator=gen)
+        pools0.append(p)
+
+    def step(pools, recs, outs, stream):
+        for l in range(L):
+            kda.kda_verify(layer, *tok.args(), cu, pools[l], si, recs[l], outs[l], stream=stream,
+                           max_seqlen=4)
+        kda.kda_commit_layers([layer] * L, cu, pools, si, recs, nacc, stream=stream)
+
+    def fresh():
+        return ([p.clone() for p in pools0], [dev_records(rows, H, Q, fill=SENT) for _ in range(L)],
+                [torch.zeros((ntok, H, 128), dtype=torch.bfloat16, device=DEV) for _ in range(L)])
+
+    pe, re_, oe = fresh()
+    step(pe, re_, oe, None)
+    torch.cuda.synchronize()
+
+    pg, rg, og = fresh()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(pg, rg, og, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(pg, rg, og, torch.cuda.current_stream())
+    for rep in range(4):
+        for l in range(L):
+            pg[l].copy_(pools0[l])
+            og[l].zero_()
+            for t in (rg[l].k, rg[l].v, rg[l].g, rg[l].beta):
+                t.view(torch.int16).fill_(np.int16(np.uint16(SENT).view(np.int16)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert torch.equal(bits(og[l]), bits(oe[l])), f"layer {l}: o differs on replay {rep}"
+            assert torch.equal(bits(pg[l]), bits(pe[l])), f"layer {l}: pool differs on replay {rep}"
+            assert torch.equal(bits(rg[l].v), bits(re_[l].v)), f"layer {l}: records differ on replay {rep}"
+        _ = (pools0[0].sum() + pg[0].abs().max()).item()
+    say("  4 replays bitwise equal to eager")
