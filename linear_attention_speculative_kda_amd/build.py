@@ -13,6 +13,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "kda.hip")
+HOST_SRC = os.path.join(PKG, "csrc", "check_rows.cpp")   # host-only C++
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 
@@ -41,7 +42,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile libkda.so next to this file and return its path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, SRC, HOST_SRC, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

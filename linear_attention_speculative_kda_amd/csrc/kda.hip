@@ -44,7 +44,6 @@
 // The conv-state compaction of the commit is a separate small copy kernel
 // (16-byte spans through LDS for the dense in-place layout).
 
-#include <vector>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -1586,7 +1585,7 @@ kda_status launch_verify_short(Params& p, int max_seqlen, hipStream_t stream) {
 
 // --------------------------------------------------------------- C ABI ----
 
-kda_status check_align(const kda_align* a, int num_rows) {
+static kda_status check_align(const kda_align* a, int num_rows) {
   if (!a) return KDA_OK;
   if (num_rows > 0 && (!a->block_table || !a->num_computed)) return KDA_ERR_NULL;
   if (a->width < 1 || a->block_size < 1 || a->row_stride < a->width) return KDA_ERR_SHAPE;
@@ -1606,7 +1605,7 @@ AlignRef align_ref(const kda_align* a) {
 }
 
 // Elements spanned by one layer's conv state: the last element's offset + 1.
-long long conv_span(const kda_conv_state* c, int conv_dim, int width) {
+static long long conv_span(const kda_conv_state* c, int conv_dim, int width) {
   return (long long)(c->num_blocks - 1) * c->block_stride + (long long)(conv_dim - 1) * c->dim_stride +
          (long long)(width - 1) * c->token_stride + 1;
 }
@@ -1614,7 +1613,7 @@ long long conv_span(const kda_conv_state* c, int conv_dim, int width) {
 // Checks shared by the multi-layer calls: every layer valid, the same head
 // count, the same record shape, one state-index array, and no two layers'
 // pools or records overlapping each other or (with `pending`) the counts.
-kda_status check_layers(const kda_layer* layers, const kda_pool* pools, const kda_records* recs,
+static kda_status check_layers(const kda_layer* layers, const kda_pool* pools, const kda_records* recs,
                         int num_layers, int num_rows, const int32_t* pending) {
   if (!layers || !pools || !recs) return KDA_ERR_NULL;
   if (num_layers < 1 || num_layers > kMaxLayers || num_rows < 0) return KDA_ERR_SHAPE;
@@ -1970,43 +1969,6 @@ const char* kda_status_string(kda_status status) {
     case KDA_ERR_METADATA: return "KDA_ERR_METADATA: a row breaks a precondition";
   }
   return "unknown kda_status";
-}
-
-kda_status kda_check_rows(const int32_t* cu_seqlens, int32_t num_rows, int32_t num_tokens,
-                          const int32_t* state_indices, int32_t num_slots,
-                          const int32_t* record_rows, int32_t rec_rows, int32_t max_seqlen,
-                          int32_t* bad_row, int32_t* issue) {
-  if (bad_row) *bad_row = -1;
-  if (issue) *issue = KDA_ROW_OK;
-  if (num_rows < 0 || num_tokens < 0 || num_slots < 0 || max_seqlen < 0) return KDA_ERR_SHAPE;
-  if (num_rows == 0) return KDA_OK;
-  if (!cu_seqlens || !state_indices) return KDA_ERR_NULL;
-  std::vector<unsigned char> slot_used((size_t)num_slots, 0);
-  std::vector<unsigned char> rec_used(rec_rows > 0 ? (size_t)rec_rows : 0, 0);
-  auto fail = [&](int row, kda_row_issue what) {
-    if (bad_row) *bad_row = row;
-    if (issue) *issue = what;
-    return KDA_ERR_METADATA;
-  };
-  for (int i = 0; i < num_rows; ++i) {
-    const int slot = state_indices[i];
-    if (slot <= 0) continue;   // a skipped row
-    const long long bos = cu_seqlens[i], eos = cu_seqlens[i + 1];
-    if (bos < 0 || eos < bos || eos > num_tokens) return fail(i, KDA_ROW_SPAN);
-    if (max_seqlen > 0 && eos - bos > max_seqlen) return fail(i, KDA_ROW_WINDOW);
-    if (slot >= num_slots) return fail(i, KDA_ROW_SLOT_RANGE);
-    if (slot_used[slot]) return fail(i, KDA_ROW_SLOT_DUP);
-    slot_used[slot] = 1;
-    if (rec_rows >= 0) {
-      const int r = record_rows ? record_rows[i] : i;
-      if (r < -1 || r >= rec_rows) return fail(i, KDA_ROW_RECORD_RANGE);
-      if (r >= 0) {
-        if (rec_used[r]) return fail(i, KDA_ROW_RECORD_DUP);
-        rec_used[r] = 1;
-      }
-    }
-  }
-  return KDA_OK;
 }
 
 const char* kda_build_info(void) {
