@@ -334,14 +334,33 @@ __device__ __forceinline__ int row_in_tile(int rr, const Ctx& c) {
   return (rr * NWAVES + c.wave) * 8 + c.grp;
 }
 
-template <int R, int BV>
+// A 16-byte load of state; NT: non-temporal (streamed: the line is not kept
+// in the caches, nor allocated in the MALL). The verify reads each
+// checkpoint once, and the commit reads each once before overwriting it
+// whole, so their state loads stream and no longer evict lines that other
+// kernels will read or write back. Only where a wave's 8-lane groups read
+// whole 128-byte lines (load_tile): the matrix-core layout reads 64 bytes of
+// a line per instruction, and streaming its loads fetched lines twice
+// (deep-draft verify 144.7 -> 154 us).
+template <bool NT>
+__device__ __forceinline__ float4 ld_state4(const float* src) {
+  if constexpr (NT) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v x = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(src));
+    return make_float4(x.x, x.y, x.z, x.w);
+  } else {
+    return *reinterpret_cast<const float4*>(src);
+  }
+}
+
+template <int R, int BV, bool NT = false>
 __device__ __forceinline__ void load_tile(float (&S)[R][16], const float* sbase, const Ctx& c) {
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     const float* src = sbase + (c.tile * BV + row_in_tile(rr, c)) * KD + c.p8 * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 x = *reinterpret_cast<const float4*>(src + j * 32);
+      const float4 x = ld_state4<NT>(src + j * 32);
       S[rr][4 * j + 0] = x.x; S[rr][4 * j + 1] = x.y; S[rr][4 * j + 2] = x.z; S[rr][4 * j + 3] = x.w;
     }
   }
@@ -699,7 +718,7 @@ __device__ __forceinline__ int mfma_row(int blk, int wave, int lane) {
   return blk * (NWAVES * 16) + wave * 16 + (lane & 15);
 }
 
-template <int RB>
+template <int RB, bool NT = false>
 __device__ __forceinline__ void load_tile_mfma(float4 (&S)[RB][8], const float* tile_base,
                                                int wave, int lane) {
   const int ch = 4 * (lane >> 4);
@@ -707,7 +726,7 @@ __device__ __forceinline__ void load_tile_mfma(float4 (&S)[RB][8], const float* 
   for (int blk = 0; blk < RB; ++blk) {
     const float* src = tile_base + mfma_row(blk, wave, lane) * KD + ch;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) S[blk][c] = *reinterpret_cast<const float4*>(src + 16 * c);
+    for (int c = 0; c < 8; ++c) S[blk][c] = ld_state4<NT>(src + 16 * c);
   }
 }
 
@@ -932,7 +951,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       if (!(gl > 0 && bos == row * gl && nmain == gl)) stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
       __builtin_amdgcn_sched_barrier(0);
       float S[R][16];
-      load_tile<R, BV>(S, sbase, c);
+      load_tile<R, BV, MODE == kVerify>(S, sbase, c);
       __builtin_amdgcn_sched_barrier(0);
       stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0, false);
       lds_barrier();
@@ -986,7 +1005,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
                                                              : (nmain < WCH ? nmain : WCH));
   __builtin_amdgcn_sched_barrier(0);
   float S[R][16];
-  load_tile<R, BV>(S, sbase, c);
+  load_tile<R, BV, MODE == kVerify || MODE == kCommit>(S, sbase, c);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- fold: replay records into the state (commit, deferred fold) --------
