@@ -345,7 +345,9 @@ __device__ __forceinline__ int row_in_tile(int rr, const Ctx& c) {
 // stream the new state out (store_tile<..., true>): nothing reads it back
 // before the next step, and a write that stays dirty in the MALL is written
 // back later while other kernels stream their own state (12-layer decode
-// step 77.4 -> 75.6 us per layer).
+// step 77.4 -> 75.6 us per layer). With both, the deferred verify streams
+// its state loads as well (decode deferred flow 64.7 -> 57.1 us per layer;
+// with its stores cached, streaming its loads alone had not paid).
 template <bool NT>
 __device__ __forceinline__ float4 ld_state4(const float* src) {
   if constexpr (NT) {
@@ -962,7 +964,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       if (!(gl > 0 && bos == row * gl && nmain == gl)) stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
       __builtin_amdgcn_sched_barrier(0);
       float S[R][16];
-      load_tile<R, BV, MODE == kVerify>(S, sbase, c);
+      load_tile<R, BV, true>(S, sbase, c);
       __builtin_amdgcn_sched_barrier(0);
       stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0, false);
       lds_barrier();
@@ -987,7 +989,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       stage_load<MODE, BV>(rv, p, c, false, 0, nmain);
       __builtin_amdgcn_sched_barrier(0);
       float S[R][16];
-      load_tile<R, BV>(S, sbase, c);
+      load_tile<R, BV, true>(S, sbase, c);
       __builtin_amdgcn_sched_barrier(0);
       stage_compute<MODE, BV, CH>(st, rf, p, c, true, 0);
       lds_barrier();
@@ -1017,7 +1019,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
                                                              : (nmain < WCH ? nmain : WCH));
   __builtin_amdgcn_sched_barrier(0);
   float S[R][16];
-  load_tile<R, BV, MODE == kVerify || MODE == kCommit>(S, sbase, c);
+  load_tile<R, BV, MODE != kRecurrent>(S, sbase, c);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- fold: replay records into the state (commit, deferred fold) --------
