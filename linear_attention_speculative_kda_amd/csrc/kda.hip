@@ -441,8 +441,10 @@ __device__ __forceinline__ void stage_load(Raw<BV>& x, const Params& p, const Ct
   x.q = fold ? make_uint2(0, 0) : *reinterpret_cast<const uint2*>(q + 4 * l32);
 #pragma unroll
   for (int e = 0; e < VPL; ++e) x.v[e] = v[c.tile * BV + l32 * VPL + e];
-  const uint16_t bv = *b;
-  x.b = (l32 == 0) ? bv : (uint16_t)0;
+  // kept as loaded (every use is by lane 0 of the half-wave): a select here
+  // would make the wave wait for all of these loads before issuing the next
+  // ones (the row metadata, the state tile)
+  x.b = *b;
 }
 
 // Write a staged window token's raw inputs to its record row (the first Q
