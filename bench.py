@@ -441,7 +441,11 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": kernels[dom]["gbs"] / PEAK_HBM_GBS,
-            "traffic": measured_traffic(dom, args.workload),
+            # the counter runs used the default step (12 layers, in-place
+            # commit in one launch); other shapes of the commit move other bytes
+            "traffic": measured_traffic(dom, args.workload)
+                       if dom == "kda_verify" or (L == 12 and align is None and not args.per_layer_commit)
+                       else None,
         },
         "kernels": kernels,
         "ms_per_layer_step": ms_layer,
