@@ -30,11 +30,13 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_verify_commit(batch, pool_np, nacc=None, sample_rows=None):
+def run_verify_commit(batch, pool_np, nacc=None, sample_rows=None, bench_launch=False):
     """Run verify + commit on the GPU and in the oracle; compare.
 
     sample_rows: oracle only on these rows (others are skipped on the oracle
-    side and not compared)."""
+    side and not compared). bench_launch: the calls as the benchmark makes
+    them (the verify with the window bound, so the short kernels; the commit
+    through the multi-layer kernel)."""
     B, H, Q = batch.num_rows, batch.H, batch.Q
     nacc = batch.num_accepted if nacc is None else nacc
     ntok = batch.tokens.num_tokens
@@ -50,12 +52,16 @@ def run_verify_commit(batch, pool_np, nacc=None, sample_rows=None):
     o = torch.full((ntok, H, 128), 0, dtype=torch.int16, device=DEV)
     o.fill_(np.int16(np.uint16(SENT).view(np.int16)))
     o = o.view(torch.bfloat16)
-    kda.kda_verify(L, *toks.args(), cu, pool, si, rec, o)
+    bound = int(batch.seq_lens().max()) if bench_launch else None
+    kda.kda_verify(L, *toks.args(), cu, pool, si, rec, o, max_seqlen=bound)
     torch.cuda.synchronize()
     assert torch.equal(pool.view(torch.int32), pool_before.view(torch.int32)), "verify wrote the pool"
     o_gpu = bits_host(o)
     rec_gpu = records_host(rec)
-    kda.kda_commit(L, cu, pool, si, rec, to_dev(nacc.astype(np.int32)))
+    if bench_launch:
+        kda.kda_commit_layers([L], cu, [pool], si, [rec], to_dev(nacc.astype(np.int32)))
+    else:
+        kda.kda_commit(L, cu, pool, si, rec, to_dev(nacc.astype(np.int32)))
     torch.cuda.synchronize()
     pool_gpu = pool.cpu().numpy()
     # ---- oracle
@@ -258,6 +264,18 @@ def test_full_size_sampled_parity(name):
     rng = np.random.default_rng(99)
     sample = sorted(rng.choice(batch.num_rows, size=6, replace=False).tolist())
     run_verify_commit(batch, pool, sample_rows=sample)
+
+
+@pytest.mark.parametrize("name", ["decode", "deep", "ragged"])
+def test_full_size_sampled_parity_bench_launch(name):
+    """The benchmark's kernels against the oracle at full size: the verify
+    with the window bound (short kernels, predicted spans) and the commit
+    through the multi-layer kernel, on sampled rows."""
+    batch = make_batch(name)
+    pool = full_pool(batch)
+    rng = np.random.default_rng(98)
+    sample = sorted(rng.choice(batch.num_rows, size=6, replace=False).tolist())
+    run_verify_commit(batch, pool, sample_rows=sample, bench_launch=True)
 
 
 @pytest.mark.parametrize("name", ["decode", "deep", "ragged"])
