@@ -332,8 +332,8 @@ const char* kda_status_string(kda_status status);
  * Rows with state_indices[i] <= 0 are skipped rows and pass; for the others:
  * a well-formed span within num_tokens, T_i <= max_seqlen when max_seqlen > 0
  * (the window bound of kda_tokens), a slot below num_slots and not shared
- * with another row (distinct slots, as the pages' one checkpoint per request
- * requires), and a record row (record_rows[i], or i when record_rows is NULL)
+ * with another row (distinct slots: one checkpoint state per request, pages:
+ * recoverssm.py, module docstring), and a record row (record_rows[i], or i when record_rows is NULL)
  * that is -1 (the scratch row: nothing is recorded) or below rec_rows and
  * not shared with another row. rec_rows < 0 skips the record-row checks.
  * Returns KDA_OK, or KDA_ERR_METADATA with *bad_row = the first offending row
