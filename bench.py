@@ -29,6 +29,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -65,9 +66,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30   # the plain copy timed below: 1 GiB read + 1 GiB written
 
 
-def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_hash(text: str | None = None) -> str:
+    """sha256 of the kernel source without its comments and blank lines:
+    counter data stays valid across edits that change no code."""
+    if text is None:
+        with open(KERNEL_SOURCE, encoding="utf-8") as f:
+            text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def kernel_key(name: str) -> str:

@@ -32,6 +32,13 @@
 //    dot products per value row and a T x T triangular recurrence, no state
 //    stepping and no state write (a window longer than one chunk advances
 //    the state in registers from one chunk to the next).
+//  * With the caller's bound on the windows (kda_tokens.max_seqlen), verify
+//    runs short kernels without the long-window code (fewer registers, more
+//    resident waves); the 4-token ones issue the window's token loads at the
+//    predicted uniform span before the row metadata arrives.
+//  * The state is streamed: the verify's tile loads and the commit's and
+//    deferred fold's loads and stores are non-temporal, since every
+//    checkpoint is touched once per kernel and step.
 //  * Matrix cores only for the verify of 8-token chunks, where the 16 dot
 //    products per value row bound the vector lanes (fp32 MFMA). Elsewhere the
 //    work per state element is a handful of FMAs against a state read once
