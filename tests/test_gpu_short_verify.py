@@ -56,12 +56,14 @@ def same_records(a, b, what):
         assert np.array_equal(getattr(a, f), getattr(b, f)), f"{what}: records.{f}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "deep", "ragged"])
-def test_short_verify_same_bits_as_general(name):
-    batch = make_batch(name)
+@pytest.mark.parametrize("name,B", [("tiny", None), ("decode", None), ("decode", 128),
+                                    ("deep", None), ("ragged", None)])
+def test_short_verify_same_bits_as_general(name, B):
+    # decode at B=128 (4096 row-heads): the 128-row tiles of the 4-token kernels
+    batch = make_batch(name, B=B)
     T = batch.seq_lens()
     bound = int(T.max())
-    say(f"short verify vs general: {name} max_seqlen={bound}")
+    say(f"short verify vs general: {name} B={batch.num_rows} max_seqlen={bound}")
     pool = random_pool(batch)
     o_g, r_g = run_verify(batch, pool, batch.cu_seqlens, None)
     o_s, r_s = run_verify(batch, pool, batch.cu_seqlens, bound)
