@@ -31,6 +31,13 @@ What it computes (sources are the four web pages on the method):
   after the last committed token goes to the block holding that token and the
   state at a crossed block boundary to that boundary's block; and the
   conv-state compaction of the same commit (``_compact_conv_state_kernel``).
+* The stock speculative path that RecoverSSM replaces (recoverssm.py module
+  docstring; kda.py, ``_forward``, its spec branch into the fused recurrent
+  kernel with a row of state indices per request; recoverssm.py,
+  ``_replay_indices_kernel``, which states how that kernel uses the row): the
+  recurrence from the state in column num_accepted - 1 of the row, storing
+  the state after token t into the block of column t; see
+  ``kda_recurrent_spec``.
 * The deferred commit of the page "vllm.models.kimi_k3.nvidia.specialized_decode
   .recoverssm.context" (``KDADeferredCommitContext.commit`` / ``flush``,
   ``KDARecoverSSMDeferred``): commit turns n' into ``pending[record_row]``
@@ -291,6 +298,57 @@ def kda_recurrent(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indice
         _store_state(pool, slot, S)
 
 
+def spec_source_column(num_accepted, i: int, cols: int) -> int:
+    """Column of row i's state-index row that holds its initial state:
+    num_accepted[i] - 1, the state after the last token accepted in the
+    previous step (recoverssm.py, ``_replay_indices_kernel``: the stock
+    kernel reads its initial state at column num_accepted - 1). Counts are
+    clamped to 1..cols (a reading: the pages pass at least one accepted token,
+    the bonus token, and never more than the row holds); no counts: column 0."""
+    if num_accepted is None:
+        return 0
+    return min(max(int(num_accepted[i]), 1), int(cols)) - 1
+
+
+def kda_recurrent_spec(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_table,
+                       num_accepted, o) -> None:
+    """The stock full-state speculative step (recoverssm.py module docstring:
+    it keeps 1 + num_spec recurrent states per request and writes one full
+    state per verified token; kda.py ``_forward``: the spec branch calls the
+    fused recurrent kernel with a [rows, columns] table of state indices and
+    the accepted counts; recoverssm.py ``_replay_indices_kernel``: that
+    kernel reads its initial state at column num_accepted - 1 and stores the
+    state after token t to the block of column t unless it is the null block).
+
+    state_table int32 [rows, cols]. For each row i with T_i > 0 whose source
+    block s = state_table[i, spec_source_column(...)] is in (0, num_slots):
+    run the T_i tokens from pool[s], write o for each, and after token t
+    (t < cols) store the state into pool[state_table[i, t]] when that block
+    is in (0, num_slots). The initial state is read before anything is
+    stored, so a column may name the source block itself. Rows whose blocks
+    overlap another row's are outside the contract."""
+    N, ntok, H = state_table.shape[0], q.shape[0], q.shape[1]
+    cols = state_table.shape[1]
+    K = q.shape[2]
+    nslots = pool.shape[0]
+    for i in range(N):
+        bos, T = _row_span(cu_seqlens, i, ntok)
+        src = int(state_table[i, spec_source_column(num_accepted, i, cols)])
+        if T == 0 or not _slot_ok(src, nslots):
+            continue
+        S = _load_state(pool, src)
+        for t in range(T):
+            tok = bos + t
+            q_hat, k_hat, vv, gg, bb = _prepare(layer, H, K, q[tok], k[tok], v[tok],
+                                                g[tok], beta[tok])
+            S, out = kda_step(S, q_hat, k_hat, vv, gg, bb)
+            o[tok] = f64_to_bf16_bits(out)
+            if t < cols:
+                dst = int(state_table[i, t])
+                if _slot_ok(dst, nslots):
+                    _store_state(pool, dst, S)
+
+
 def _write_records(rec: Records, ri: int, k, v, g, beta, bos: int, T: int) -> None:
     # Records are the raw bf16 inputs (``_verify_kernel``); the window holds Q
     # tokens, so tokens at or beyond Q are not recorded.
@@ -397,7 +455,8 @@ def commit_plan(cu_seqlens, num_tokens: int, num_accepted, state_indices, Q: int
 
 
 def kda_commit_align(layer: Layer, cu_seqlens, num_tokens: int, pool, state_indices,
-                     rec: Records, num_accepted, align: Align, record_rows=None) -> None:
+                     rec: Records, num_accepted, align: Align, record_rows=None,
+                     pending=None, eager=None) -> None:
     """The commit in align mode (``_replay_indices_kernel`` and the commit's
     replay): replay the first n' records from the source block; the state
     after the first boundary-length records goes to the boundary block when
@@ -405,13 +464,31 @@ def kda_commit_align(layer: Layer, cu_seqlens, num_tokens: int, pool, state_indi
     records goes to the final block. A row is skipped without a source, a
     final block (not null and inside the pool) or a record row. Blocks that
     are out of the pool are not written (a reading for memory safety).
-    Destination blocks are assumed to be no other row's source."""
+    Destination blocks are assumed to be no other row's source.
+
+    With ``pending`` (the deferred commit in align mode: recoverssm.context,
+    ``KDADeferredCommitContext.commit`` takes the block table together with
+    ``pending``, and ``KDARecoverSSMDeferred.eager`` marks the rows committed
+    after sampling, in align mode those near a block boundary): the counts
+    are written as in ``kda_commit`` (pending[r] = 0 for eager rows, else n'
+    for rows with a source, n' > 0 and a record row, else 0) and only the
+    eager rows commit now, in align mode as above. The other rows' replay
+    waits for the next deferred verify, which folds it in place at the row's
+    slot, so a caller defers only rows whose final block is their source and
+    that cross no block boundary (a reading: the pages print neither
+    ``_defer_commit_kernel`` nor the fold's plan)."""
     plan = commit_plan(cu_seqlens, num_tokens, num_accepted, state_indices, rec.window, align)
     nslots = pool.shape[0]
     for i in range(len(state_indices)):
         n, final, bnd, blen = (int(x) for x in plan[i])
         src = int(state_indices[i])
         ri = _record_index(record_rows, i, rec.rows)
+        if pending is not None:
+            now = eager is not None and bool(eager[i])
+            if ri > 0:
+                pending[ri - 1] = 0 if now else (n if (n > 0 and _slot_ok(src, nslots)) else 0)
+            if not now:
+                continue
         if n == 0 or ri == 0 or not _slot_ok(src, nslots) or not _slot_ok(final, nslots):
             continue
         S = _load_state(pool, src)

@@ -44,9 +44,26 @@ MUTATIONS = {
                                     "vals = conv[src, :, n:n + history].copy()"),
     "conv boundary takes the final window": ("bvals = conv[src, :, blen - 1:blen - 1 + history].copy()",
                                              "bvals = conv[src, :, n - 1:n - 1 + history].copy()"),
+    "spec source column not minus one": ("return min(max(int(num_accepted[i]), 1), int(cols)) - 1",
+                                         "return min(max(int(num_accepted[i]), 1), int(cols) - 1)"),
+    "spec state stored one column late": ("                dst = int(state_table[i, t])",
+                                          "                dst = int(state_table[i, t + 1]) if t + 1 < cols else 0"),
+    "spec null column stored": ("                if _slot_ok(dst, nslots):",
+                                "                if dst < nslots:"),
+    "spec state stored before the token": (
+        "            S, out = kda_step(S, q_hat, k_hat, vv, gg, bb)\n            o[tok] = f64_to_bf16_bits(out)\n"
+        "            if t < cols:\n                dst = int(state_table[i, t])\n"
+        "                if _slot_ok(dst, nslots):\n                    _store_state(pool, dst, S)\n",
+        "            if t < cols:\n                dst = int(state_table[i, t])\n"
+        "                if _slot_ok(dst, nslots):\n                    _store_state(pool, dst, S)\n"
+        "            S, out = kda_step(S, q_hat, k_hat, vv, gg, bb)\n            o[tok] = f64_to_bf16_bits(out)\n"),
+    "align deferred commits every row": ("            if not now:\n                continue", "            pass"),
+    "align deferred pending counts invalid rows": (
+        "pending[ri - 1] = 0 if now else (n if (n > 0 and _slot_ok(src, nslots)) else 0)",
+        "pending[ri - 1] = 0 if now else n"),
 }
 
-PIN_FILES = ("test_oracle.py", "test_oracle_commit_align.py")
+PIN_FILES = ("test_oracle.py", "test_oracle_commit_align.py", "test_oracle_spec.py")
 
 
 def _run_pins(tmp_path, src):
