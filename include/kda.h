@@ -110,10 +110,16 @@ typedef struct kda_tokens {
    * 0 when unknown (pages: kda.py, _forward, where the speculative window's
    * maximum query length num_spec + 1 is known on the host and handed to the
    * short convolution). Used by kda_verify only: with 1 <= max_seqlen <= 8 it
-   * runs kernels built for windows of at most that many tokens, and a row
-   * longer than max_seqlen is then skipped like a row without a slot
-   * (nothing of it is written). Larger values run the general kernels.
-   * Negative -> KDA_ERR_SHAPE (every call). */
+   * runs kernels built for windows of at most that many tokens; larger
+   * values run the general kernels. A row with a slot and T_i > max_seqlen
+   * breaks the caller's guarantee and is not verified: every output of its
+   * tokens is set to NaN (bf16 0x7FC0) and so is the beta record of each of
+   * its recorded tokens (the first min(T_i, Q)); its other records are not
+   * written. The error thus shows in the outputs, and a commit that replays
+   * such a row (n' > 0) stores NaN, never a plausible checkpoint (pages:
+   * recoverssm.py, _check_config fails where a commit would otherwise go
+   * wrong silently). kda_check_rows reports such rows on the host
+   * (KDA_ROW_WINDOW). Negative -> KDA_ERR_SHAPE (every call). */
   int32_t max_seqlen;
 } kda_tokens;
 
@@ -157,6 +163,15 @@ typedef struct kda_align {
   int32_t block_size;           /* tokens per block, >= 1 */
 } kda_align;
 
+/* The block ids of the stock speculative step (host struct of device
+ * pointers): per request row, one block per window position. */
+typedef struct kda_spec_table {
+  const int32_t* indices;       /* [num_rows, cols] int32, row stride row_stride elements */
+  int64_t row_stride;           /* >= cols */
+  int32_t cols;                 /* >= 1: 1 + num_spec positions */
+  const int32_t* num_accepted;  /* [num_rows] int32, or NULL (the source is column 0) */
+} kda_spec_table;
+
 /* One layer's conv state (host struct of a device pointer): 16-bit elements
  * [num_blocks, channels, width] with element strides. */
 typedef struct kda_conv_state {
@@ -183,14 +198,44 @@ kda_status kda_recurrent(const kda_layer* layer, const kda_tokens* tokens,
                          const kda_pool* pool, uint16_t* o, hipStream_t stream);
 
 /*
+ * kda_recurrent_spec -- the stock speculative step that RecoverSSM replaces,
+ * one full state stored per verified token (pages: recoverssm.py, module
+ * docstring: the stock path keeps 1 + num_spec states per request; kda.py,
+ * _forward, its speculative branch into the fused recurrent kernel with a
+ * row of state indices per request and the accepted counts; recoverssm.py,
+ * _replay_indices_kernel: that kernel reads the initial state at column
+ * num_accepted - 1 and stores the state after token t to column t unless
+ * it is the null block). Kept as the baseline whose state traffic the
+ * verify + commit removes.
+ * For each row i with T_i > 0: the source column is
+ * c = min(max(num_accepted[i], 1), cols) - 1 (0 when num_accepted is NULL)
+ * and the source block table->indices[i][c]; a source outside
+ * (0, num_slots) skips the row (nothing written). Otherwise run the T_i
+ * tokens from the source with the per-token code of kda_recurrent, write o
+ * for each token, and after token t < cols store the state into block
+ * indices[i][t] when it lies in (0, num_slots). The source is read before
+ * any store, so a column may name the source itself. The state in column t
+ * has the bits kda_recurrent stores after the same t + 1 tokens.
+ *   pool: pool->state_indices is not used (may be NULL).
+ *   o: [num_tokens, H, 128] bf16.
+ * Blocks named by one row must not be named by another row. Errors as
+ * kda_recurrent, plus: table NULL -> KDA_ERR_NULL; cols < 1 or
+ * row_stride < cols -> KDA_ERR_SHAPE.
+ */
+kda_status kda_recurrent_spec(const kda_layer* layer, const kda_tokens* tokens,
+                              const kda_pool* pool, const kda_spec_table* table,
+                              uint16_t* o, hipStream_t stream);
+
+/*
  * kda_verify -- speculative verify from the checkpoint (pages: recoverssm.py,
  * module docstring and _verify_kernel / kda_recoverssm_verify). For each valid
  * row: run its T_i window tokens from the checkpoint, write o, and write the
  * raw k, v, g, beta of tokens 0..min(T_i, Q)-1 to record row r, where
  * r = record_rows[i] (record_rows == NULL: r = i, which needs
  * num_rows <= rec->rows, else KDA_ERR_CAPACITY). The pool is read only: no
- * state is written. With tokens->max_seqlen in 1..8 the rows longer than it
- * are skipped (see kda_tokens); the others give the same bits as without it.
+ * state is written. With tokens->max_seqlen in 1..8 the rows within the
+ * bound give the same bits as without it, and the rows longer than it get
+ * NaN outputs and NaN beta records (see kda_tokens).
  * Errors as kda_recurrent, plus: records overlapping o, the pool or the
  * token arrays -> KDA_ERR_ALIAS; misaligned records -> KDA_ERR_ALIGN.
  */
@@ -260,8 +305,16 @@ kda_status kda_verify_deferred(const kda_layer* layer, const kda_tokens* tokens,
  *   sees the row (a slot at or beyond that pool's num_slots counts as
  *   skipped there).
  *   align (host struct, may be NULL): the align mode above, which writes
- *   the final (and boundary) block instead of the source; only without
- *   pending (deferred mode with align -> KDA_ERR_UNSUPPORTED).
+ *   the final (and boundary) block instead of the source. With pending as
+ *   well (the deferred commit in align mode; pages: recoverssm.context,
+ *   KDADeferredCommitContext.commit takes the block table with pending, and
+ *   KDARecoverSSMDeferred.eager marks the rows committed after sampling, in
+ *   align mode those near a block boundary): the eager rows commit now in
+ *   align mode; the other rows only get their count,
+ *   pending[r] = (slot in (0, num_slots) and n' > 0) ? n' : 0, and the next
+ *   kda_verify_deferred replays them in place at their slot, so a caller
+ *   defers only rows whose final block is their slot and that cross no
+ *   block boundary.
  * Errors as kda_commit, plus: num_layers outside 1..16, layers that differ
  * in num_heads or record shape, or pools with different state_indices ->
  * KDA_ERR_SHAPE; a layer's pool or records overlapping another layer's pool

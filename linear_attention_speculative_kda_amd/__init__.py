@@ -20,6 +20,7 @@ from .kda import (  # noqa: F401
     kda_flush,
     kda_flush_layers,
     kda_recurrent,
+    kda_recurrent_spec,
     kda_verify,
     kda_verify_deferred,
 )

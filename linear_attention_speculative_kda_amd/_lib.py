@@ -82,6 +82,15 @@ class KdaAlign(ctypes.Structure):
     ]
 
 
+class KdaSpecTable(ctypes.Structure):
+    _fields_ = [
+        ("indices", c_ptr),
+        ("row_stride", ctypes.c_int64),
+        ("cols", ctypes.c_int32),
+        ("num_accepted", c_ptr),
+    ]
+
+
 class KdaConvState(ctypes.Structure):
     _fields_ = [
         ("state", c_ptr),
@@ -114,6 +123,8 @@ def load() -> ctypes.CDLL:
     lib.kda_recurrent.argtypes = [P(KdaLayer), P(KdaTokens), P(KdaPool), c_ptr, c_ptr]
     lib.kda_verify.argtypes = [P(KdaLayer), P(KdaTokens), P(KdaPool), P(KdaRecords), c_ptr,
                                c_ptr, c_ptr]
+    lib.kda_recurrent_spec.argtypes = [P(KdaLayer), P(KdaTokens), P(KdaPool), P(KdaSpecTable),
+                                       c_ptr, c_ptr]
     lib.kda_commit.argtypes = [P(KdaLayer), c_ptr, ctypes.c_int32, P(KdaPool), P(KdaRecords),
                                c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
     lib.kda_verify_deferred.argtypes = [P(KdaLayer), P(KdaTokens), P(KdaPool), P(KdaRecords),
@@ -126,7 +137,7 @@ def load() -> ctypes.CDLL:
                                      c_ptr, ctypes.c_int32, P(KdaAlign), c_ptr]
     lib.kda_flush_layers.argtypes = [P(KdaLayer), P(KdaPool), P(KdaRecords), ctypes.c_int32,
                                      ctypes.c_int32, c_ptr, c_ptr, c_ptr]
-    for fn in ("kda_recurrent", "kda_verify", "kda_commit", "kda_verify_deferred",
+    for fn in ("kda_recurrent", "kda_recurrent_spec", "kda_verify", "kda_commit", "kda_verify_deferred",
                "kda_commit_layers", "kda_flush_layers", "kda_conv_compact"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kda_check_rows.argtypes = [c_ptr, ctypes.c_int32, ctypes.c_int32, c_ptr, ctypes.c_int32,

@@ -67,7 +67,7 @@ constexpr int NWAVES = 4;
 constexpr int CH = 8;          // tokens staged in LDS per chunk
 constexpr int MAX_WINDOW = 64;
 
-enum Mode : int { kRecurrent = 0, kVerify = 1, kCommit = 2, kDeferred = 3 };
+enum Mode : int { kRecurrent = 0, kVerify = 1, kCommit = 2, kDeferred = 3, kSpec = 4 };
 
 // Align mode of the commit: a row of block ids per request row, the tokens
 // each request had cached before the step, and the tokens per block.
@@ -131,6 +131,7 @@ struct Params {
   int num_rows;
   int num_tokens;
   int guess_len;           // short verify: predicted uniform window length, 0: none
+  int max_seqlen;          // short verify: the caller's bound on every window
   // pool
   float* state;
   long long slot_stride;
@@ -160,6 +161,11 @@ struct Params {
   int flush;               // deferred fold only: every window is empty, no token is read
   int pending_skip;        // commit, deferred mode: this launch does not write pending
   AlignRef align;          // commit: block table (align.bt == nullptr: in place)
+  // stock speculative step (kSpec): a row of block ids per request row
+  const int* spec_idx;
+  long long spec_stride;
+  int spec_cols;
+  const int* spec_acc;     // accepted counts (nullptr: the source is column 0)
 };
 
 // Per-layer pointers of a multi-layer launch (the rest of Params is shared:
@@ -296,14 +302,28 @@ struct Stage {
 // The chunk-form verify additionally keeps, for the window's tokens t and
 // s <= t (Gamma_t = the decay product over tokens 1..t, P(s,t) the product
 // over tokens s+1..t, both diagonal over key channels):
-//   al[t] = Gamma_t k^_t,  ga[t] = Gamma_t q^_t,
+//   al(t) = Gamma_t k^_t,  ga(t) = Gamma_t q^_t,
 //   M[t][s] = k^_s . P(s,t) k^_t  (s < t),   N[t][s] = k^_s . P(s,t) q^_t.
+// The 2 NT decayed vectors are the rows of av, in the order the matrix-core
+// dot products take them as the rows of their A operand: row
+// 8 (t / 4) + t % 4 is al(t), the same plus 4 is ga(t); row 2 NT is zero
+// (the A rows of tokens beyond the window read it). A row is padded to 132
+// floats (528 bytes), so that 16 lanes reading one 16-byte column of 16
+// rows hit 16 different bank groups.
+constexpr int kAvStride = KD + 4;
+
+__device__ __forceinline__ int al_row(int t) { return 8 * (t >> 2) + (t & 3); }
+__device__ __forceinline__ int ga_row(int t) { return 8 * (t >> 2) + 4 + (t & 3); }
+
 template <int BV, int NT>
 struct StageChunk : Stage<BV, NT> {
-  float al[NT][KD];
-  float ga[NT][KD];
+  float av[2 * NT + 1][kAvStride];
   float M[NT][NT];
   float N[NT][NT];
+  __device__ float* al(int t) { return av[al_row(t)]; }
+  __device__ float* ga(int t) { return av[ga_row(t)]; }
+  __device__ const float* al(int t) const { return av[al_row(t)]; }
+  __device__ const float* ga(int t) const { return av[ga_row(t)]; }
 };
 
 // Per-workgroup constants.
@@ -509,10 +529,14 @@ __device__ __forceinline__ void stage_compute(Stage<BV, NT>& st, const Raw<BV>& 
 }
 
 // The per-token recurrence over m staged tokens, state in registers. With
-// `out`, token t's output goes to o[tok0 + t].
-template <int R, int BV, int NT>
+// `out`, token t's output goes to o[tok0 + t]. SPEC (the stock speculative
+// step): after token t the state also goes to the block of column
+// col0 + t of the row's block ids `spec_row`, unless that column is past
+// the row or names the null block (or one outside the pool).
+template <int R, int BV, int NT, bool SPEC = false>
 __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT>& st, const Params& p,
-                                           const Ctx& c, int m, bool out, long long tok0) {
+                                           const Ctx& c, int m, bool out, long long tok0,
+                                           const int* spec_row = nullptr, int col0 = 0) {
   for (int t = 0; t < m; ++t) {
     float kh[16], dk[16];
     lds_row16(st.kh[t], c.p8, kh);
@@ -537,6 +561,15 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
       for (int rr = 0; rr < R; ++rr) {
         const float ov = row_dot(S[rr], qh);
         if (c.p8 == 0) orow[row_in_tile(rr, c)] = f32_to_bf16(ov);
+      }
+    }
+    if constexpr (SPEC) {
+      const int col = col0 + t;
+      if (col < p.spec_cols) {
+        const int dst = scalar_load(spec_row + col);
+        if (dst > 0 && dst < p.num_slots)
+          store_tile<R, BV, true>(S, p.state + (long long)dst * p.slot_stride +
+                                         (long long)c.head * KD * KD, c);
       }
     }
   }
@@ -574,10 +607,11 @@ __device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c,
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
         gam = gam * dd[t];
-        st.al[t][ch] = gam * kk[t];
-        st.ga[t][ch] = gam * qq[t];
+        st.al(t)[ch] = gam * kk[t];
+        st.ga(t)[ch] = gam * qq[t];
       }
     }
+    st.av[2 * NT][ch] = 0.0f;
   }
   // Coefficients: the T(T+1)/2 pairs (s, t), s <= t, numbered t(t+1)/2 + s,
   // are dealt to the 8 half-waves; each lane covers 4 key channels. The pair
@@ -638,10 +672,10 @@ __device__ __forceinline__ void chunk_dots(const float (&S)[R][16], const StageC
   for (int t = 0; t < TMAX; ++t) {
     if (t < T) {
       float v16[16];
-      lds_row16(st.al[t], c.p8, v16);
+      lds_row16(st.al(t), c.p8, v16);
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) a[rr][t] = row_dot(S[rr], v16);
-      lds_row16(st.ga[t], c.p8, v16);
+      lds_row16(st.ga(t), c.p8, v16);
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) b[rr][t] = row_dot(S[rr], v16);
     }
@@ -714,103 +748,113 @@ __device__ __forceinline__ void chunk_verify(float (&S)[R][16], StageChunk<BV, N
 
 // ------------------------------------------------- matrix-core chunk verify --
 //
-// With 8-token chunks the 2T = 16 dot products per value row dominate the
-// verify's vector-ALU time. They form a small matrix product D = A B, A the
-// 16 decayed vectors (Gamma_t k^_t, Gamma_t q^_t; rows of unused tokens
-// read as zero) over the key channels and B the state tile (key channel x
-// value row), which v_mfma_f32_16x16x4_f32 computes in fp32 (fp32 products,
-// fp32 accumulation). Each wave owns 16-row blocks of the tile, RB of them.
+// The 2T dot products per value row (a_t with al(t), b_t with ga(t)) form a
+// small matrix product D = A B: A the decayed vectors (rows of av) over the
+// key channels, B the state tile (key channel x value row). fp32 MFMA
+// (v_mfma_f32_16x16x4_f32: fp32 products, fp32 sums) computes it, so the
+// vector lanes keep only the staging, the coefficients and the recurrence
+// (with the dot products on the vector lanes, they were the verify's bound:
+// taking them out took the decode-size verify from 34.5 to 25.1 us).
 //
-// Operand layout for lane l, i = l % 16, g = l / 16: A[i][g] and B[g][i]
-// are one register each; register r of D holds D[4g + r][i]. The state is
-// loaded straight into the B layout: lane l holds value row i of its block
-// and, for chunk c = 0..7, the key channels 16c + 4g + e (e = 0..3) with one
-// 16-byte load; component e feeds the chunk's e-th instruction, and A is
-// read from LDS with the same channel mapping (only the order of the terms
-// of each sum differs from the vector form). Row i of A is vector
-// t = 4 (i / 8) + i % 4: Gamma_t k^_t for i % 8 < 4, Gamma_t q^_t otherwise;
-// so D register r of lane group g holds a_t (g even) or b_t (g odd) for
-// t = 4 (g / 2) + r. The recurrence then runs one value row per lane, after
-// the a_t, b_t of each row are regrouped through LDS.
+// The state stays in the streamed vector layout (whole 128-byte lines per
+// load: a lane group of 8 holds one value row). The MFMA operand layout
+// wants one value row per lane (lane l: row l % 16, key group l / 16), so
+// each wave moves its rows through its own 2 KiB of LDS, 32 key channels at
+// a time: block blk of a wave = its register sets 2 blk and 2 blk + 1 (16
+// value rows, MFMA row i = 8 (set parity) + group); the chunk of 4 keys
+// that lane p8 of a group holds goes to unit p8 ^ ((i / 2) % 8) of row i
+// (16-byte units, 8 per row), which keeps both the writes and the reads
+// free of bank conflicts. Lane (i, g) then reads the units of key chunks
+// 2g and 2g + 1 of row i, and the A values of the same keys from av row i.
+// For T <= 4 only A rows 0..7 exist (rows 8..15 read as zero).
+//
+// D register r of lane (i, g) holds A row 4 g + r against value row i:
+// a_t (g even) or b_t (g odd) for t = 4 (g / 2) + r. The rows' a_t, b_t are
+// regrouped through the same per-wave LDS and the recurrence runs one value
+// row per lane.
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// Value row of the tile held by (block blk, wave, lane).
-__device__ __forceinline__ int mfma_row(int blk, int wave, int lane) {
-  return blk * (NWAVES * 16) + wave * 16 + (lane & 15);
+// Per-wave LDS of the matrix-core path: the transpose buffer (16 rows x 32
+// keys), then, once the products are done, the regrouped a_t, b_t of the
+// wave's rows (20 floats per row: a_0..a_7, b_0..b_7, padding).
+template <int R>
+struct XBuf {
+  static constexpr int kFloats = (16 * 32 > 16 * (R / 2) * 20) ? 16 * 32 : 16 * (R / 2) * 20;
+  float w[NWAVES][kFloats];
+};
+
+// The tile row of MFMA row i of block blk (register sets 2 blk, 2 blk + 1).
+__device__ __forceinline__ int xrow(int blk, int i, const Ctx& c) {
+  return ((2 * blk + (i >> 3)) * NWAVES + c.wave) * 8 + (i & 7);
 }
 
-template <int RB, bool NT = false>
-__device__ __forceinline__ void load_tile_mfma(float4 (&S)[RB][8], const float* tile_base,
-                                               int wave, int lane) {
-  const int ch = 4 * (lane >> 4);
-#pragma unroll
-  for (int blk = 0; blk < RB; ++blk) {
-    const float* src = tile_base + mfma_row(blk, wave, lane) * KD + ch;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) S[blk][c] = ld_state4<NT>(src + 16 * c);
-  }
-}
-
-// D for each block; two accumulators per block (even and odd chunks) keep
-// two independent chains in flight.
-template <int RB, int BV, int NT>
-__device__ __forceinline__ void mfma_dots(const float4 (&S)[RB][8], const StageChunk<BV, NT>& st,
-                                          int T, int lane, floatx4 (&D)[RB]) {
+template <int R, int BV, int NT>
+__device__ __forceinline__ void xpose_dots(const float (&S)[R][16], const StageChunk<BV, NT>& st,
+                                           float* xb, const Ctx& c, int T, floatx4 (&D)[R / 2]) {
+  const int lane = c.tid & 63;
   const int i = lane & 15, g = lane >> 4;
   const int t = 4 * (i >> 3) + (i & 3);
-  const bool live = t < T;
-  const float* vec = (((i >> 2) & 1) ? st.ga[live ? t : 0] : st.al[live ? t : 0]) + 4 * g;
-  floatx4 acc[RB][2];
+  const bool live = i < 2 * NT && t < T;
+  const float* arow = st.av[live ? i : 2 * NT] + 8 * g;
+  const int grp = c.grp, p8 = c.p8;
+  float* w0 = xb + grp * 32 + 4 * (p8 ^ ((grp >> 1) & 7));
+  float* w1 = xb + (8 + grp) * 32 + 4 * (p8 ^ (((8 + grp) >> 1) & 7));
+  const float* r0 = xb + i * 32 + 4 * ((2 * g) ^ ((i >> 1) & 7));
+  const float* r1 = xb + i * 32 + 4 * ((2 * g + 1) ^ ((i >> 1) & 7));
 #pragma unroll
-  for (int blk = 0; blk < RB; ++blk) {
-    acc[blk][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-    acc[blk][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int blk = 0; blk < R / 2; ++blk) {
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float4 a = *reinterpret_cast<const float4*>(vec + 16 * c);
-    if (!live) a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int blk = 0; blk < RB; ++blk) {
-      floatx4& d = acc[blk][c & 1];
-      d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, S[blk][c].x, d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, S[blk][c].y, d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, S[blk][c].z, d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, S[blk][c].w, d, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      // this lane's 4 keys 32 q + 4 p8 .. of its two rows of the block
+      *reinterpret_cast<float4*>(w0) =
+          make_float4(S[2 * blk][4 * q], S[2 * blk][4 * q + 1], S[2 * blk][4 * q + 2], S[2 * blk][4 * q + 3]);
+      *reinterpret_cast<float4*>(w1) = make_float4(S[2 * blk + 1][4 * q], S[2 * blk + 1][4 * q + 1],
+                                                   S[2 * blk + 1][4 * q + 2], S[2 * blk + 1][4 * q + 3]);
+      // (a wave's LDS operations run in order: the reads see the writes)
+      const float4 b0 = *reinterpret_cast<const float4*>(r0);
+      const float4 b1 = *reinterpret_cast<const float4*>(r1);
+      const float4 a0 = *reinterpret_cast<const float4*>(arow + 32 * q);
+      const float4 a1 = *reinterpret_cast<const float4*>(arow + 32 * q + 4);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.x, b0.x, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.x, b1.x, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.y, b0.y, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.y, b1.y, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.z, b0.z, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.z, b1.z, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.w, b0.w, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.w, b1.w, acc1, 0, 0, 0);
     }
+    D[blk] = acc0 + acc1;
   }
-#pragma unroll
-  for (int blk = 0; blk < RB; ++blk) D[blk] = acc[blk][0] + acc[blk][1];
 }
 
-// The triangular recurrence and the outputs, one value row per lane: the
-// wave's D registers go to LDS (row-major, a_0..a_7 then b_0..b_7 per value
-// row), and lane l < 16 RB takes row mfma_row(l / 16, wave, l), one of the
-// rows this wave computed, so only the wave's own LDS writes are read.
-template <int RB, int BV, int TMAX, int NT>
-__device__ __forceinline__ void mfma_recur_rows(const floatx4 (&D)[RB], const StageChunk<BV, NT>& st,
-                                                float (*dx)[17], const Params& p, const Ctx& c,
-                                                int lane, int T, long long tok0) {
+// The triangular recurrence and the outputs, one value row per lane, after
+// the a_t, b_t of the wave's rows are regrouped through its LDS (lane
+// 16 blk + i takes MFMA row i of block blk).
+template <int R, int BV, int TMAX, int NT>
+__device__ __forceinline__ void xpose_recur(const floatx4 (&D)[R / 2], const StageChunk<BV, NT>& st,
+                                            float* xb, const Params& p, const Ctx& c, int T,
+                                            long long tok0) {
+  const int lane = c.tid & 63;
   const int g = lane >> 4;
   const int col = (g & 1) * 8 + 4 * (g >> 1);
+  if (TMAX > 4 || g < 2) {
 #pragma unroll
-  for (int blk = 0; blk < RB; ++blk) {
-    float* d = dx[mfma_row(blk, c.wave, lane)] + col;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) d[r] = D[blk][r];
+    for (int blk = 0; blk < R / 2; ++blk)
+      *reinterpret_cast<float4*>(xb + (blk * 16 + (lane & 15)) * 20 + col) =
+          make_float4(D[blk].x, D[blk].y, D[blk].z, D[blk].w);
   }
-  // LDS operations of one wave complete in order; the reads below see the
-  // writes above (wait for them anyway before the reads)
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (lane >= 16 * RB) return;
-  const int vloc = mfma_row(lane >> 4, c.wave, lane);
-  const float* row = dx[vloc];
+  if (lane >= 16 * (R / 2)) return;
+  const int blk = lane >> 4, i = lane & 15;
+  const int vloc = xrow(blk, i, c);
+  const float* rowd = xb + lane * 20;
   float a[TMAX], b[TMAX], u[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {
-    a[t] = row[t];
-    b[t] = row[8 + t];
+    a[t] = rowd[t];
+    b[t] = rowd[8 + t];
   }
   uint16_t* orow = p.o + (tok0 * c.H + c.head) * KD + c.tile * BV + vloc;
 #pragma unroll
@@ -818,13 +862,62 @@ __device__ __forceinline__ void mfma_recur_rows(const floatx4 (&D)[RB], const St
     if (t < T) {
       float x = st.vt[t][vloc] - a[t];
 #pragma unroll
-      for (int s = 0; s < t; ++s) x = fmaf(-st.M[t][s], u[s], x);
+      for (int s2 = 0; s2 < t; ++s2) x = fmaf(-st.M[t][s2], u[s2], x);
       u[t] = st.bt[t] * x;
       float y = b[t];
 #pragma unroll
-      for (int s = 0; s <= t; ++s) y = fmaf(st.N[t][s], u[s], y);
+      for (int s2 = 0; s2 <= t; ++s2) y = fmaf(st.N[t][s2], u[s2], y);
       orow[(long long)t * c.H * KD] = f32_to_bf16(y);
     }
+  }
+}
+
+// One chunk of T <= TMAX window tokens from the state in registers, the
+// dot products on the matrix cores (tiles of 64 or 128 value rows).
+template <int R, int BV, int TMAX, int NT>
+__device__ __forceinline__ void chunk_verify_mfma(const float (&S)[R][16], StageChunk<BV, NT>& st,
+                                                  XBuf<R>& xb, const Params& p, const Ctx& c, int T,
+                                                  long long tok0) {
+  static_assert(R >= 2, "the matrix-core path takes 16 value rows per wave");
+  coef_phase<BV, TMAX, NT>(st, c, T);
+  lds_barrier();
+  floatx4 D[R / 2];
+  xpose_dots<R, BV, NT>(S, st, xb.w[c.wave], c, T, D);
+  xpose_recur<R, BV, TMAX, NT>(D, st, xb.w[c.wave], p, c, T, tok0);
+}
+
+// A chunk that fits the window: the matrix-core form where the tile allows
+// it, else the vector form.
+template <int R, int BV, int TMAX, int NT>
+__device__ __forceinline__ void chunk_verify_one(float (&S)[R][16], StageChunk<BV, NT>& st,
+                                                 const Params& p, const Ctx& c, int T, long long tok0) {
+  if constexpr (R >= 2) {
+    __shared__ XBuf<R> xb;
+    chunk_verify_mfma<R, BV, TMAX, NT>(S, st, xb, p, c, T, tok0);
+  } else {
+    chunk_verify<R, BV, TMAX, NT>(S, st, p, c, T, tok0);
+  }
+}
+
+// A row longer than the caller's window bound reached a short verify kernel:
+// a broken precondition that must not pass silently. Its outputs become NaN
+// (this workgroup's value rows of every token of the row) and so do the
+// beta records of its recorded tokens (the tile-0 workgroup), so that a
+// commit replaying them cannot produce a plausible checkpoint (recoverssm.py
+// page, _check_config: fail where a commit would otherwise go wrong
+// silently). Nothing else of the row is written.
+constexpr uint16_t kBf16NaN = 0x7FC0;
+
+template <int BV>
+__device__ __forceinline__ void poison_row(const Params& p, const Ctx& c, int T) {
+  for (int i = c.tid; i < T * BV; i += NTHREADS) {
+    const int t = i / BV, vr = i - t * BV;
+    p.o[((long long)(c.bos + t) * c.H + c.head) * KD + c.tile * BV + vr] = kBf16NaN;
+  }
+  if (c.tile == 0) {
+    const int n = T < p.Q ? T : p.Q;
+    for (int t = c.tid; t < n; t += NTHREADS)
+      p.rb[((long long)c.ri * c.H + c.head) * p.Q + t] = kBf16NaN;
   }
 }
 
@@ -846,20 +939,38 @@ __device__ __forceinline__ int commit_count(const Params& p, int row, int T) {
   n = n < T ? n : T;
   return n < p.Q ? n : p.Q;
 }
+// The stock speculative step reads a row's initial state from column
+// num_accepted - 1 of its block ids (counts clamped to 1..cols; no counts:
+// column 0).
+__device__ __forceinline__ int spec_source(const Params& p, int row) {
+  int col = 0;
+  if (p.spec_acc) {
+    int n = p.spec_acc[row];
+    n = n < 1 ? 1 : n;
+    n = n > p.spec_cols ? p.spec_cols : n;
+    col = n - 1;
+  }
+  return p.spec_idx[(long long)row * p.spec_stride + col];
+}
+
 __device__ __forceinline__ bool commit_now(const Params& p, int row) {
   return p.pending == nullptr || (p.eager != nullptr && p.eager[row] != 0);
 }
 
-// SHORT (verify only): a kernel for windows of at most TMAX tokens, the
-// caller's bound; it has no code for longer windows, whose registers would
-// set the allocation of the whole kernel, and it skips longer rows. (The
+// SHORT (verify only): a kernel for windows within the caller's bound
+// p.max_seqlen <= TMAX; it has no code for longer windows, whose registers
+// would set the allocation of the whole kernel, and it poisons the outputs
+// and beta records of a row longer than the bound (poison_row). (The
 // same cut in the deferred verify, 106 -> 96 VGPRs at 64-row tiles, ran 3%
 // slower: the extra resident workgroups contend in its fold and store.)
 template <int MODE, int R, int TMAX, bool SHORT = false>
 __device__ __forceinline__ void kda_block(const Params& p, int b) {
   constexpr int BV = R * NWAVES * 8;   // value rows per workgroup
   constexpr bool kChunk = (MODE == kVerify || MODE == kDeferred);
-  using StageT = typename std::conditional<kChunk, StageChunk<BV, CH>, Stage<BV, CH>>::type;
+  // tokens staged at a time: the verify stages one chunk of its window
+  // (TMAX); the replays of the other modes stage up to CH records or tokens
+  constexpr int SNT = MODE == kVerify ? TMAX : CH;
+  using StageT = typename std::conditional<kChunk, StageChunk<BV, SNT>, Stage<BV, SNT>>::type;
   __shared__ StageT st;
 
   Ctx c;
@@ -896,7 +1007,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   int T = eos - bos;
   if (bos < 0 || T < 0 || (MODE != kCommit && eos > p.num_tokens)) T = 0;
   c.bos = bos;
-  const int slot = p.slots[row];
+  const int slot = MODE == kSpec ? spec_source(p, row) : p.slots[row];
   const bool slot_ok = slot > 0 && slot < p.num_slots;
   const int r = p.record_rows ? p.record_rows[row] : row;
   c.ri = (r >= 0 && r < p.rec_rows) ? r + 1 : 0;   // storage index, 0 = scratch
@@ -922,8 +1033,10 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
     const bool valid = slot_ok && n > 0 && c.ri > 0 && final_ok;
     const bool now = commit_now(p, row);
     if (p.pending) {
+      // a deferred replay runs in place at the row's slot (the next
+      // deferred verify), so the align blocks do not enter the count
       if (!p.pending_skip && c.ri > 0 && c.head == 0 && c.tile == 0 && c.tid == 0)
-        p.pending[c.ri - 1] = now ? 0 : (valid ? n : 0);
+        p.pending[c.ri - 1] = now ? 0 : ((slot_ok && n > 0) ? n : 0);
     }
     nfold = (valid && now) ? n : 0;
   } else if (MODE == kDeferred) {
@@ -940,34 +1053,13 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   c.A = exp_hw(scalar_load(p.a_log + c.head));
   float* sbase = p.state + (long long)slot * p.slot_stride + (long long)c.head * KD * KD;
   if (fbase == nullptr) fbase = sbase;
-  const bool chunk = kChunk && nmain <= TMAX;
+  const bool chunk = kChunk && nmain <= (SHORT ? p.max_seqlen : TMAX);
 
   // Verify of a window that fits one chunk: straight-line code from the
   // loads to the outputs. A control-flow join between the state loads and
   // their first use lets the compiler copy the state registers there, which
   // waits for the whole tile before the token staging can start.
   // (kda_verify_deferred takes it too for rows with nothing to fold.)
-  if constexpr (MODE == kVerify && TMAX == CH && R >= 2) {
-    if (chunk) {   // 8-token chunks: the dot products on the matrix cores
-      constexpr int RB = R / 2;
-      const int lane = c.tid & 63;
-      stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
-      __builtin_amdgcn_sched_barrier(0);
-      float4 S[RB][8];
-      load_tile_mfma<RB>(S, sbase + c.tile * BV * KD, c.wave, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0, false);
-      lds_barrier();
-      coef_phase<BV, TMAX, CH>(st, c, nmain);
-      lds_barrier();
-      floatx4 D[RB];
-      mfma_dots<RB, BV, CH>(S, st, nmain, lane, D);
-      __shared__ float dx[BV][17];
-      mfma_recur_rows<RB, BV, TMAX, CH>(D, st, dx, p, c, lane, nmain, (long long)bos);
-      store_records<BV>(raw, p, c, 0);
-      return;
-    }
-  }
   if constexpr (MODE == kVerify || MODE == kDeferred) {
     if (chunk && nfold == 0) {
       if (!(gl > 0 && bos == row * gl && nmain == gl)) stage_load<MODE, BV>(raw, p, c, false, 0, nmain);
@@ -975,15 +1067,18 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       float S[R][16];
       load_tile<R, BV, true>(S, sbase, c);
       __builtin_amdgcn_sched_barrier(0);
-      stage_compute<MODE, BV, CH>(st, raw, p, c, false, 0, false);
+      stage_compute<MODE, BV, SNT>(st, raw, p, c, false, 0, false);
       lds_barrier();
-      chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos);
+      chunk_verify_one<R, BV, TMAX, SNT>(S, st, p, c, nmain, (long long)bos);
       // the records last: stores issued behind the state loads would make
       // later register reuse wait for those loads
       store_records<BV>(raw, p, c, 0);
       return;
     }
-    if constexpr (SHORT) return;   // a window longer than the caller's bound
+    if constexpr (SHORT) {   // a window longer than the caller's bound
+      poison_row<BV>(p, c, nmain);
+      return;
+    }
   }
 
   // Deferred verify of a row with a pending replay (it fits one chunk: the
@@ -1000,15 +1095,15 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       float S[R][16];
       load_tile<R, BV, true>(S, sbase, c);
       __builtin_amdgcn_sched_barrier(0);
-      stage_compute<MODE, BV, CH>(st, rf, p, c, true, 0);
+      stage_compute<MODE, BV, SNT>(st, rf, p, c, true, 0);
       lds_barrier();
-      seq_tokens<R, BV, CH>(S, st, p, c, nfold, false, 0);
+      seq_tokens<R, BV, SNT>(S, st, p, c, nfold, false, 0);
       store_tile<R, BV, true>(S, fbase, c);
       if (nmain > 0) {
         lds_barrier();   // the fold's staged tokens are consumed
-        stage_compute<MODE, BV, CH>(st, rv, p, c, false, 0, false);
+        stage_compute<MODE, BV, SNT>(st, rv, p, c, false, 0, false);
         lds_barrier();
-        chunk_verify<R, BV, TMAX, CH>(S, st, p, c, nmain, (long long)bos);
+        chunk_verify_one<R, BV, TMAX, SNT>(S, st, p, c, nmain, (long long)bos);
         store_records<BV>(rv, p, c, 0);
       }
       return;
@@ -1024,7 +1119,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   const int seg0 = (bbase != nullptr) ? blen : nfold;
   // window tokens per pass: one chunk (TMAX) in the chunked modes
   constexpr int WCH = kChunk ? TMAX : CH;
-  stage_load<MODE, BV>(raw, p, c, first_fold, 0, first_fold ? (seg0 < CH ? seg0 : CH)
+  stage_load<MODE, BV>(raw, p, c, first_fold, 0, first_fold ? (seg0 < SNT ? seg0 : SNT)
                                                              : (nmain < WCH ? nmain : WCH));
   __builtin_amdgcn_sched_barrier(0);
   float S[R][16];
@@ -1035,12 +1130,12 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   if (nfold > 0) {
     for (int c0 = 0; c0 < nfold;) {
       const int end = (bbase != nullptr && c0 < blen) ? blen : nfold;
-      const int m = (end - c0) < CH ? (end - c0) : CH;
+      const int m = (end - c0) < SNT ? (end - c0) : SNT;
       if (c0 > 0) stage_load<MODE, BV>(raw, p, c, true, c0, m);
       lds_barrier();  // the previous chunk is consumed
-      stage_compute<MODE, BV, CH>(st, raw, p, c, true, c0);
+      stage_compute<MODE, BV, SNT>(st, raw, p, c, true, c0);
       lds_barrier();
-      seq_tokens<R, BV, CH>(S, st, p, c, m, false, 0);
+      seq_tokens<R, BV, SNT>(S, st, p, c, m, false, 0);
       c0 += m;
       if (bbase != nullptr && c0 == blen) store_tile<R, BV, kStreamStore>(S, bbase, c);
     }
@@ -1065,19 +1160,23 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
                      "+v"(cl.wave));
         if (c0 > 0) stage_load<MODE, BV>(raw, p, cl, false, c0, m);
         lds_barrier();
-        stage_compute<MODE, BV, CH>(st, raw, p, cl, false, c0);
+        stage_compute<MODE, BV, SNT>(st, raw, p, cl, false, c0);
         lds_barrier();
-        chunk_verify<R, BV, TMAX, CH>(S, st, p, cl, m, (long long)bos + c0, c0 + m < nmain);
+        chunk_verify<R, BV, TMAX, SNT>(S, st, p, cl, m, (long long)bos + c0, c0 + m < nmain);
       }
       return;
     }
-    for (int c0 = 0; c0 < nmain; c0 += CH) {
-      const int m = (nmain - c0) < CH ? (nmain - c0) : CH;
+    for (int c0 = 0; c0 < nmain; c0 += SNT) {
+      const int m = (nmain - c0) < SNT ? (nmain - c0) : SNT;
       if (c0 > 0) stage_load<MODE, BV>(raw, p, c, false, c0, m);
       lds_barrier();
-      stage_compute<MODE, BV, CH>(st, raw, p, c, false, c0);
+      stage_compute<MODE, BV, SNT>(st, raw, p, c, false, c0);
       lds_barrier();
-      seq_tokens<R, BV, CH>(S, st, p, c, m, true, (long long)bos + c0);
+      if constexpr (MODE == kSpec)
+        seq_tokens<R, BV, SNT, true>(S, st, p, c, m, true, (long long)bos + c0,
+                                    p.spec_idx + (long long)row * p.spec_stride, c0);
+      else
+        seq_tokens<R, BV, SNT>(S, st, p, c, m, true, (long long)bos + c0);
     }
     if (MODE == kRecurrent) store_tile<R, BV>(S, sbase, c);
   }
@@ -1477,7 +1576,7 @@ int tile_rows_for(int mode, long long pairs) {
     }
   }
   if (forced > 0) return forced;
-  if (mode == kCommit || mode == kRecurrent) return 32;
+  if (mode == kCommit || mode == kRecurrent || mode == kSpec) return 32;
   if (mode == kVerify && pairs >= 4096) return 128;
   return pairs >= 512 ? 64 : 32;
 }
@@ -1619,6 +1718,7 @@ kda_status launch(Params& p, hipStream_t stream) {
 kda_status launch_verify_short(Params& p, int max_seqlen, hipStream_t stream) {
   const int g = p.num_tokens % p.num_rows == 0 ? p.num_tokens / p.num_rows : 0;
   p.guess_len = (g >= 1 && g <= max_seqlen) ? g : 0;
+  p.max_seqlen = max_seqlen;
   if (max_seqlen <= 4) return launch_t<kVerify, 4, true>(p, stream);
   return launch_t<kVerify, CH, true>(p, stream);
 }
@@ -1735,6 +1835,37 @@ kda_status kda_recurrent(const kda_layer* layer, const kda_tokens* tokens, const
   p.o = o;
   p.Q = 1;
   return launch<kRecurrent>(p, stream);
+}
+
+kda_status kda_recurrent_spec(const kda_layer* layer, const kda_tokens* tokens, const kda_pool* pool,
+                              const kda_spec_table* table, uint16_t* o, hipStream_t stream) {
+  kda_status s = check_layer(layer);
+  if (s != KDA_OK) return s;
+  const int H = layer->num_heads;
+  if ((s = check_tokens(tokens, H)) != KDA_OK) return s;
+  if (!table) return KDA_ERR_NULL;
+  if ((s = check_pool(pool, H, 0)) != KDA_OK) return s;   // state_indices: not used
+  if (table->cols < 1 || table->row_stride < table->cols) return KDA_ERR_SHAPE;
+  if (tokens->num_rows == 0) return KDA_OK;
+  if (!table->indices) return KDA_ERR_NULL;
+  if (!o && tokens->num_tokens > 0) return KDA_ERR_NULL;
+  if (!aligned(o, 2)) return KDA_ERR_ALIGN;
+  Ranges in;
+  token_ranges(tokens, H, in);
+  in.add(pool_range(pool, H));
+  const Range orange = range_of(o, (long long)tokens->num_tokens * H * KD * 2);
+  if (any_overlap(orange, in)) return KDA_ERR_ALIAS;
+  Params p = base_params(layer);
+  set_tokens(p, tokens);
+  set_pool(p, pool);
+  p.slots = nullptr;
+  p.o = o;
+  p.Q = 1;
+  p.spec_idx = table->indices;
+  p.spec_stride = table->row_stride;
+  p.spec_cols = table->cols;
+  p.spec_acc = table->num_accepted;
+  return launch<kSpec>(p, stream);
 }
 
 kda_status kda_verify(const kda_layer* layer, const kda_tokens* tokens, const kda_pool* pool,
@@ -1863,7 +1994,6 @@ kda_status kda_commit_layers(const kda_layer* layers, const kda_pool* pools,
   if (!cu_seqlens || (num_rows > 0 && !num_accepted)) return KDA_ERR_NULL;
   if (eager && !pending) return KDA_ERR_SHAPE;
   if ((s = check_align(align, num_rows)) != KDA_OK) return s;
-  if (align && pending) return KDA_ERR_UNSUPPORTED;
   if (num_rows == 0) return KDA_OK;
   if (!record_rows && num_rows > recs[0].rows) return KDA_ERR_CAPACITY;
   Params p = base_params(&layers[0]);

@@ -1,5 +1,5 @@
-"""Python front end of libkda: the calls of include/kda.h (recurrent, verify,
-commit, deferred verify and flush, the multi-layer commit and flush, the
+"""Python front end of libkda: the calls of include/kda.h (recurrent, the
+stock speculative step, verify, commit, deferred verify and flush, the multi-layer commit and flush, the
 conv-state compaction), taking torch tensors that live on the GPU.
 Marshalling only; the computation is in HIP.
 
@@ -225,6 +225,31 @@ def kda_recurrent(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indice
     st = lib.kda_recurrent(ctypes.byref(L), ctypes.byref(T), ctypes.byref(P),
                            _out(o, q.shape[0], H), _stream(stream))
     _lib.check("kda_recurrent", st)
+
+
+def kda_recurrent_spec(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_table,
+                       num_accepted=None, o=None, stream=None) -> None:
+    """The stock speculative step: each row runs its window from the block in
+    column num_accepted - 1 of its row of ``state_table`` (int32 [rows,
+    cols]; column 0 without counts) and stores the state after token t into
+    the block of column t (0: none). o for every token."""
+    _on_gpu(pool, layer, q, k, v, g, beta, cu_seqlens, state_table, num_accepted, o)
+    lib = _lib.load()
+    H = layer.num_heads
+    rows = cu_seqlens.numel() - 1
+    if state_table.dtype != torch.int32 or state_table.dim() != 2 or state_table.stride(1) != 1:
+        raise ValueError("state_table must be an int32 [rows, cols] tensor with unit column stride")
+    if state_table.shape[0] < rows:
+        raise ValueError(f"state_table has {state_table.shape[0]} rows, needs {rows}")
+    L, T = layer.c_struct(), _tokens(q, k, v, g, beta, cu_seqlens, H)
+    P = _pool(pool, torch.zeros(1, dtype=torch.int32, device=pool.device), H)
+    P.state_indices = None
+    tab = _lib.KdaSpecTable(indices=state_table.data_ptr(), row_stride=state_table.stride(0),
+                            cols=state_table.shape[1],
+                            num_accepted=_opt_ptr(num_accepted, torch.int32, "num_accepted", rows))
+    st = lib.kda_recurrent_spec(ctypes.byref(L), ctypes.byref(T), ctypes.byref(P), ctypes.byref(tab),
+                                _out(o, q.shape[0], H), _stream(stream))
+    _lib.check("kda_recurrent_spec", st)
 
 
 def kda_verify(layer: Layer, q, k, v, g, beta, cu_seqlens, pool, state_indices,

@@ -3,7 +3,13 @@ oracle on them, and the parity criteria.
 
 Parity criteria (fp32 state, bf16 outputs):
   state  per (slot, head): ||S_gpu - S_ref||_F <= 1e-5 * ||S_ref||_F
-  o      |o_gpu - o_ref| <= ulp_bf16(o_ref) + 1e-3, o_ref the oracle's bf16 value
+  o      the stated gate: |o_gpu - o_ref| <= ulp_bf16(o_ref) + 1e-3, o_ref the
+         oracle's bf16 value; and a tight check on every comparison:
+         |o_gpu - o_ref| <= ulp_bf16(o_ref) + 1e-5. The outputs of these
+         workloads are small (median |o| about 1e-3), where the gate's
+         absolute term alone would pass a zero output; an fp32 computation
+         of o that differs from the fp64 one only by rounding lands on the
+         oracle's bf16 value or a neighbour, which the tight check allows.
   records, untouched memory: bitwise
 """
 
@@ -14,7 +20,8 @@ import numpy as np
 from oracle import kda_ref as ref
 
 S_RTOL = 1e-5
-O_ATOL = 1e-3
+O_ATOL = 1e-3          # the stated output tolerance (the gate)
+O_ATOL_TIGHT = 1e-5    # the tight check applied alongside it
 
 
 def bf16_val(bits: np.ndarray) -> np.ndarray:
@@ -29,17 +36,43 @@ def ulp_bf16(bits: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, np.maximum(e, 1) - 127 - 7)
 
 
-def check_o(o_gpu_bits: np.ndarray, o_ref_bits: np.ndarray, mask=None, what="o") -> None:
+def o_stats(o_gpu_bits: np.ndarray, o_ref_bits: np.ndarray, mask=None) -> dict:
+    """Distance of the GPU outputs from the oracle's in bf16 steps: the
+    largest |difference| / ulp_bf16(reference), the share that is
+    bit-identical and the number compared."""
     g, r = bf16_val(o_gpu_bits), bf16_val(o_ref_bits)
-    bound = ulp_bf16(o_ref_bits) + O_ATOL
-    err = np.abs(g - r)
-    bad = err > bound
+    ulp = ulp_bf16(o_ref_bits)
+    d = np.abs(g - r) / ulp
+    same = np.asarray(o_gpu_bits, np.uint16) == np.asarray(o_ref_bits, np.uint16)
     if mask is not None:
-        bad &= mask
-    if bad.any():
-        idx = np.argwhere(bad)[:5]
-        raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance, e.g. at "
-                             f"{idx.tolist()}: gpu {g[tuple(idx[0])]} ref {r[tuple(idx[0])]}")
+        m = np.broadcast_to(mask, d.shape)
+        d, same = d[m], same[m]
+    n = int(d.size)
+    return {"n": n, "max_ulp": float(d.max()) if n else 0.0,
+            "bit_exact": float(same.mean()) if n else 1.0}
+
+
+def check_o(o_gpu_bits: np.ndarray, o_ref_bits: np.ndarray, mask=None, what="o",
+            quiet: bool = False) -> dict:
+    """Both output checks (the gate and the tight one); prints and returns
+    the ulp statistics."""
+    g, r = bf16_val(o_gpu_bits), bf16_val(o_ref_bits)
+    ulp = ulp_bf16(o_ref_bits)
+    err = np.abs(g - r)
+    for atol, kind in ((O_ATOL, "tolerance"), (O_ATOL_TIGHT, "tight check")):
+        bad = err > ulp + atol
+        if mask is not None:
+            bad &= mask
+        if bad.any():
+            idx = np.argwhere(bad)[:5]
+            raise AssertionError(f"{what}: {int(bad.sum())} elements outside the {kind} "
+                                 f"(1 ulp + {atol:g}), e.g. at {idx.tolist()}: gpu "
+                                 f"{g[tuple(idx[0])]} ref {r[tuple(idx[0])]}")
+    st = o_stats(o_gpu_bits, o_ref_bits, mask)
+    if not quiet:
+        print(f"  {what}: {st['n']} outputs, max {st['max_ulp']:.2f} ulp, "
+              f"{100 * st['bit_exact']:.2f}% bit-exact", flush=True)
+    return st
 
 
 def check_state(S_gpu: np.ndarray, S_ref: np.ndarray, what="state") -> float:

@@ -134,6 +134,31 @@ def test_verify_rejects_aliasing():
     assert verify(R=r) == E["KDA_ERR_ALIAS"]
 
 
+def spec(L=None, T=None, P=None, tab=None, o=O, null_table=False):
+    lib = _lib.load()
+    if tab is None:
+        tab = _lib.KdaSpecTable(indices=A + 0x600000, row_stride=4, cols=4, num_accepted=A + 0x700000)
+    return lib.kda_recurrent_spec(ctypes.byref(L or layer()), ctypes.byref(T or tokens()),
+                                  ctypes.byref(P or pool(state_indices=None)),
+                                  None if null_table else ctypes.byref(tab), o, None)
+
+
+def test_recurrent_spec_validation():
+    assert spec(null_table=True) == E["KDA_ERR_NULL"]
+    assert spec(tab=_lib.KdaSpecTable(indices=A, row_stride=4, cols=0)) == E["KDA_ERR_SHAPE"]
+    assert spec(tab=_lib.KdaSpecTable(indices=A, row_stride=3, cols=4)) == E["KDA_ERR_SHAPE"]
+    assert spec(tab=_lib.KdaSpecTable(indices=0, row_stride=4, cols=4)) == E["KDA_ERR_NULL"]
+    assert spec(L=layer(head_dim=64)) == E["KDA_ERR_UNSUPPORTED"]
+    assert spec(T=tokens(q=0)) == E["KDA_ERR_NULL"]
+    assert spec(P=pool(state=A + 0x1000004, state_indices=None)) == E["KDA_ERR_ALIGN"]
+    assert spec(o=0) == E["KDA_ERR_NULL"]
+    assert spec(o=A + 0x1000000 + 1024) == E["KDA_ERR_ALIAS"]     # o inside the pool
+    assert spec(o=A + 0x100000 + 64) == E["KDA_ERR_ALIAS"]        # o inside the tokens
+    # no rows: nothing to do, even without a table array
+    assert spec(T=tokens(n_rows=0, num_tokens=0),
+                tab=_lib.KdaSpecTable(indices=0, row_stride=4, cols=4)) == E["KDA_OK"]
+
+
 def test_empty_batch_is_a_no_op():
     # num_rows == 0 returns OK before anything is enqueued (no GPU touched)
     assert verify(T=tokens(n_rows=0, num_tokens=0)) == E["KDA_OK"]
@@ -261,8 +286,8 @@ def test_commit_layers_align_validation():
     assert commit_layers(align=align(width=0)) == E["KDA_ERR_SHAPE"]
     assert commit_layers(align=align(block_size=0)) == E["KDA_ERR_SHAPE"]
     assert commit_layers(align=align(row_stride=3)) == E["KDA_ERR_SHAPE"]
-    # the deferred mode has no align form
-    assert commit_layers(align=align(), pending=A + 0x700000) == E["KDA_ERR_UNSUPPORTED"]
+    # the deferred mode in align form passes the host checks (no rows: no launch)
+    assert commit_layers(align=align(), pending=A + 0x700000, n_rows=0) == E["KDA_OK"]
     assert commit_layers(align=align(), n_rows=0) == E["KDA_OK"]
 
 
@@ -314,7 +339,7 @@ def test_struct_layouts_match_the_header(tmp_path):
         pytest.skip("no host C compiler")
     structs = {"kda_layer": _lib.KdaLayer, "kda_tokens": _lib.KdaTokens, "kda_pool": _lib.KdaPool,
                "kda_records": _lib.KdaRecords, "kda_align": _lib.KdaAlign,
-               "kda_conv_state": _lib.KdaConvState}
+               "kda_conv_state": _lib.KdaConvState, "kda_spec_table": _lib.KdaSpecTable}
     lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "kda.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')

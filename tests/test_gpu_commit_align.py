@@ -77,6 +77,61 @@ def test_commit_align_against_oracle(layers):
                 assert np.array_equal(got[b], pools0[l][b]), f"layer {l} block {b} written"
 
 
+@pytest.mark.parametrize("B,H,layers", [(12, 4, 1), (12, 4, 3), (2049, 1, 1)])
+def test_commit_align_deferred_against_oracle(B, H, layers):
+    """The deferred commit in align mode: the eager rows commit into their
+    align blocks now, the others only record their counts (row list for up
+    to 2048 rows, the full grid beyond)."""
+    say(f"align deferred commit vs oracle: B={B} H={H} layers={layers}")
+    run = make_deferred(B=B, H=H, layers=layers, steps=1)
+    rng = np.random.default_rng(12)
+    width, bs = 4, 2
+    nblocks = run.num_slots + width * B
+    bt = (run.num_slots + np.arange(B * width, dtype=np.int32)).reshape(B, width)
+    bt[3, :] = 0
+    cached = rng.integers(-1, 9, size=B).astype(np.int32)
+    eager = (rng.random(B) < 0.5).astype(np.uint8)
+    si, cu, rr = to_dev(run.state_indices), to_dev(run.cu_seqlens), to_dev(run.record_rows)
+    nacc_np = run.num_accepted(0)
+    Ls, pools0, recs = [], [], []
+    for l in range(layers):
+        p = run.params[l]
+        Ls.append(kda.Layer(a_log=to_dev(p.a_log), g_bias=to_dev(p.g_bias), scale=run.scale,
+                            lower_bound=run.lower_bound))
+        pool = np.zeros((nblocks, H, 128, 128), np.float32)
+        pool[:run.num_slots] = run.initial_pool(l)
+        pools0.append(pool)
+        rec = dev_records(B, H, run.Q)
+        o = torch.empty((B * run.T, H, 128), dtype=torch.bfloat16, device=DEV)
+        kda.kda_verify(Ls[l], *DevTokens(run.tokens(l, 0)).args(), cu, to_dev(pool), si, rec, o,
+                       record_rows=rr)
+        recs.append(rec)
+    pools = [to_dev(p) for p in pools0]
+    pending = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    al = kda.Align(to_dev(bt), to_dev(cached), bs)
+    kda.kda_commit_layers(Ls, cu, pools, si, recs, to_dev(nacc_np), record_rows=rr,
+                          pending=pending, eager=to_dev(eager), align=al)
+    torch.cuda.synchronize()
+    oal = ref.Align(bt, cached, bs)
+    want_pending = np.full(B, -9, np.int32)
+    for l in range(layers):
+        p = run.params[l]
+        want = pools0[l].copy()
+        ref.kda_commit_align(ref.Layer(p.a_log, p.g_bias, run.scale, run.lower_bound),
+                             run.cu_seqlens, B * run.T, want, run.state_indices,
+                             records_host(recs[l]), nacc_np, oal, record_rows=run.record_rows,
+                             pending=want_pending, eager=eager)
+        got = pools[l].cpu().numpy()
+        written = np.flatnonzero(np.any(want != pools0[l], axis=(1, 2, 3)))
+        say(f"  layer {l}: {len(written)} blocks written by eager rows")
+        for b in written:
+            check_state(got[b], want[b], what=f"layer {l} block {b}")
+        same = np.ones(nblocks, bool)
+        same[written] = False
+        assert np.array_equal(got[same], pools0[l][same]), f"layer {l}: a block no row writes changed"
+    assert np.array_equal(pending.cpu().numpy(), want_pending), "pending counts"
+
+
 def test_commit_align_bits_equal_prefix_commits():
     """The final block holds the bits of a plain commit of n' records, the
     boundary block those of a plain commit of the boundary length."""

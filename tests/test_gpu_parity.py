@@ -79,9 +79,15 @@ def run_verify_commit(batch, pool_np, nacc=None, sample_rows=None, bench_launch=
     ref.kda_commit(lay, batch.cu_seqlens, ntok, pool_ref, si_ref, rec_ref, nacc)
     # ---- compare
     rows = range(B) if sample_rows is None else sample_rows
+    tok_mask = np.zeros((ntok, 1, 1), bool)
     for i in rows:
-        bos, T = int(batch.cu_seqlens[i]), int(batch.seq_lens()[i])
-        check_o(o_gpu[bos:bos + T], o_ref[bos:bos + T], what=f"o row {i}")
+        if batch.state_indices[i] > 0:
+            bos, T = int(batch.cu_seqlens[i]), int(batch.seq_lens()[i])
+            tok_mask[bos:bos + T] = True
+    check_o(o_gpu, o_ref, mask=tok_mask,
+            what=f"{batch.name}{'' if batch.lower_bound is None else ' bounded'} o, "
+                 f"{len(rows)} rows{' (bench launch)' if bench_launch else ''}")
+    for i in rows:
         assert np.array_equal(rec_gpu.k[i + 1], rec_ref.k[i + 1]), f"records k row {i}"
         assert np.array_equal(rec_gpu.v[i + 1], rec_ref.v[i + 1]), f"records v row {i}"
         assert np.array_equal(rec_gpu.g[i + 1], rec_ref.g[i + 1]), f"records g row {i}"
@@ -248,43 +254,51 @@ def test_empty_and_window_longer_than_records():
 # --------------------------------------------------------- full size ----
 
 _POOL_CACHE = {}
+FULL_SIZE = ["decode", "decode_bounded", "deep", "ragged"]
 
 
 def full_pool(batch):
-    if batch.name not in _POOL_CACHE:
+    key = (batch.name, batch.lower_bound)
+    if key not in _POOL_CACHE:
         say(f"oracle checkpoints for {batch.name} (B={batch.num_rows}, H={batch.H})")
-        _POOL_CACHE[batch.name] = oracle_prefill_pool(batch)
-    return _POOL_CACHE[batch.name]
+        _POOL_CACHE[key] = oracle_prefill_pool(batch)
+    return _POOL_CACHE[key]
 
 
-@pytest.mark.parametrize("name", ["decode", "deep", "ragged"])
+def sampled_rows(batch, seed, n=32):
+    """At least n rows, always the first and the last (every row when there
+    are no more than n)."""
+    B = batch.num_rows
+    if B <= n:
+        return list(range(B))
+    rng = np.random.default_rng(seed)
+    inner = rng.choice(np.arange(1, B - 1), size=n - 2, replace=False)
+    return sorted([0, B - 1, *inner.tolist()])
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
 def test_full_size_sampled_parity(name):
     batch = make_batch(name)
-    pool = full_pool(batch)
-    rng = np.random.default_rng(99)
-    sample = sorted(rng.choice(batch.num_rows, size=6, replace=False).tolist())
-    run_verify_commit(batch, pool, sample_rows=sample)
+    run_verify_commit(batch, full_pool(batch), sample_rows=sampled_rows(batch, 99))
 
 
-@pytest.mark.parametrize("name", ["decode", "deep", "ragged"])
+@pytest.mark.parametrize("name", FULL_SIZE)
 def test_full_size_sampled_parity_bench_launch(name):
     """The benchmark's kernels against the oracle at full size: the verify
     with the window bound (short kernels, predicted spans) and the commit
     through the multi-layer kernel, on sampled rows."""
     batch = make_batch(name)
-    pool = full_pool(batch)
-    rng = np.random.default_rng(98)
-    sample = sorted(rng.choice(batch.num_rows, size=6, replace=False).tolist())
-    run_verify_commit(batch, pool, sample_rows=sample, bench_launch=True)
+    run_verify_commit(batch, full_pool(batch), sample_rows=sampled_rows(batch, 98),
+                      bench_launch=True)
 
 
-@pytest.mark.parametrize("name", ["decode", "deep", "ragged"])
+@pytest.mark.parametrize("name", FULL_SIZE)
 def test_full_size_commit_bitexact(name):
     batch = make_batch(name)
     commit_bitexact_vs_recurrent(batch, full_pool(batch), batch.num_accepted)
 
 
-@pytest.mark.parametrize("name", ["decode", "deep", "ragged"])
+@pytest.mark.parametrize("name", FULL_SIZE)
 def test_verify_outputs_match_recurrent_outputs(name):
     """kda_verify (the chunked form against the checkpoint) and kda_recurrent
     (the per-token loop) compute the same window from the same checkpoints:

@@ -1,8 +1,8 @@
 """GPU parity of kda_verify with the caller's window bound (kda_tokens.max_seqlen):
 the short kernels, with token loads issued at a predicted uniform span,
 give the bits of the general kernels for every row within the bound, match
-the oracle, fall back correctly where the prediction fails, and skip the
-rows longer than the bound without writing anything."""
+the oracle, fall back correctly where the prediction fails, and mark the
+rows longer than the bound (NaN outputs and beta records)."""
 
 import sys
 
@@ -108,28 +108,75 @@ def test_short_verify_mispredicted_spans():
     assert np.all(o_s[~mask] == SENT), "o written outside the valid rows"
 
 
-def test_short_verify_skips_rows_longer_than_the_bound():
+NAN = 0x7FC0
+
+
+@pytest.mark.parametrize("bound", [2, 3, 4, 5, 7])
+def test_short_verify_poisons_rows_longer_than_the_bound(bound):
+    """Rows within the bound give the general kernel's bits; a row with a
+    slot and T_i > bound gets NaN outputs and NaN beta records (its other
+    records untouched), so that the commit after it stores NaN for that row
+    and nothing plausible; skipped rows stay untouched."""
     batch = make_batch("ragged", B=16, H=4)
-    lens = np.array([4, 6, 3, 4, 8, 1, 2, 4], np.int64)
+    batch.state_indices = batch.state_indices.copy()
+    batch.state_indices[6] = -1     # a long row without a slot: skipped, untouched
+    lens = np.array([bound, bound + 1, bound - 1, bound, bound + 1, 1, bound + 1, bound], np.int64)
     rows = len(lens)
     cu = np.zeros(rows + 1, np.int32)
     cu[1:] = np.cumsum(lens)
     assert cu[-1] <= batch.tokens.num_tokens
-    say(f"short verify, rows longer than the bound: lens={lens.tolist()} bound=4")
+    si = batch.state_indices[:rows]
+    say(f"short verify, rows longer than the bound: lens={lens.tolist()} bound={bound} "
+        f"slots={si.tolist()}")
     pool = random_pool(batch)
-    o_g, r_g = run_verify(batch, pool, cu, None, Q=8)
-    o_s, r_s = run_verify(batch, pool, cu, 4, Q=8)
+    Q = 8
+    o_g, r_g = run_verify(batch, pool, cu, None, Q=Q)
+    o_s, r_s = run_verify(batch, pool, cu, bound, Q=Q)
     starts = cu[:-1]
+    long_rows = []
     for i in range(rows):
         span = slice(starts[i], starts[i] + lens[i])
-        rec_row = i + 1
-        if lens[i] > 4 or batch.state_indices[i] <= 0:
-            assert np.all(o_s[span] == SENT), f"row {i}: o written"
-            assert np.all(r_s.k[rec_row] == SENT) and np.all(r_s.v[rec_row] == SENT), f"row {i}: records"
+        rr = i + 1
+        if si[i] <= 0:
+            assert np.all(o_s[span] == SENT), f"skipped row {i}: o written"
+            for f in ("k", "v", "g", "beta"):
+                assert np.all(getattr(r_s, f)[rr] == SENT), f"skipped row {i}: records.{f}"
+        elif lens[i] > bound:
+            long_rows.append(i)
+            assert np.all(o_s[span] == NAN), f"row {i} (T={lens[i]} > {bound}): o not NaN"
+            n = min(int(lens[i]), Q)
+            assert np.all(r_s.beta[rr][:, :n] == NAN), f"row {i}: beta records not NaN"
+            assert np.all(r_s.beta[rr][:, n:] == SENT), f"row {i}: beta written past the window"
+            for f in ("k", "v", "g"):
+                assert np.all(getattr(r_s, f)[rr] == SENT), f"row {i}: records.{f} written"
         else:
             assert np.array_equal(o_s[span], o_g[span]), f"row {i}: o"
             for f in ("k", "v", "g", "beta"):
-                assert np.array_equal(getattr(r_s, f)[rec_row], getattr(r_g, f)[rec_row]), f"row {i}: {f}"
+                assert np.array_equal(getattr(r_s, f)[rr], getattr(r_g, f)[rr]), f"row {i}: {f}"
+    assert long_rows, "no row above the bound has a slot"
+    # the commit after the short verify: the long rows store NaN (every
+    # element of every head), the others what the commit after the general
+    # verify stores
+    nacc = np.maximum(lens, 1).astype(np.int32)
+    pools = []
+    for bnd in (None, bound):
+        p = to_dev(pool)
+        rec = dev_records(rows, batch.H, Q, fill=SENT)
+        L = dev_layer(batch)
+        sid, cud = to_dev(si), to_dev(cu)
+        o = torch.empty((batch.tokens.num_tokens, batch.H, 128), dtype=torch.bfloat16, device=DEV)
+        kda.kda_verify(L, *DevTokens(batch.tokens).args(), cud, p, sid, rec, o, max_seqlen=bnd)
+        kda.kda_commit(L, cud, p, sid, rec, to_dev(nacc))
+        torch.cuda.synchronize()
+        pools.append(p.cpu().numpy())
+    for i in range(rows):
+        s = int(si[i])
+        if s <= 0:
+            continue
+        if i in long_rows:
+            assert np.all(np.isnan(pools[1][s])), f"row {i}: the commit stored a number"
+        else:
+            assert np.array_equal(pools[1][s], pools[0][s]), f"row {i}: committed state differs"
 
 
 def test_short_verify_eight_token_kernel_on_short_windows():

@@ -4,6 +4,7 @@ from .configs import (  # noqa: F401
     Batch,
     DeferredRun,
     CONFIG_NAMES,
+    SINGLE_CALL,
     make_batch,
     make_deferred,
     bf16_from_f32,

@@ -17,6 +17,10 @@ Workloads (K = V = 128 throughout, scale = 1/sqrt(128)):
             the recurrence is left to the caller); num_accepted ~Binomial(4,0.7).
   deep      B=256, H=32, T=8 (Q=8); checkpoints ~N(0,0.02); 1024-slot pool,
             rows in a random sample of slots 1..1023; num_accepted ~U{0..8}.
+  decode_bounded
+            the decode batch with the bounded gate, lower_bound=-5 (the same
+            draws as decode; the prefill that makes the checkpoints runs with
+            this gate too).
   ragged    B=128, H=32, T_i ~U{1..8} packed by cu_seqlens (Q=8); g_raw ~N(0,2),
             other activations ~N(0,1); bounded gate, lower_bound=-5; 256-slot
             pool; each row skipped w.p. 0.1 (slot 0 and -1 alternating);
@@ -164,9 +168,20 @@ class Batch:
         return pool
 
 
+# Variants of a workload: (base workload, lower_bound override).
+_VARIANTS = {"decode_bounded": ("decode", -5.0)}
+SINGLE_CALL = ("tiny", "decode", "decode_bounded", "deep", "ragged")
+
+
 def make_batch(name: str, B: int | None = None, H: int | None = None) -> Batch:
     """Draw one of the single-call workloads. B and H may be reduced for quick
     runs; every other part of the recipe stays the same."""
+    if name in _VARIANTS:
+        base, lb = _VARIANTS[name]
+        batch = make_batch(base, B, H)
+        batch.name = name
+        batch.lower_bound = lb
+        return batch
     seed = _SEEDS[name]
     meta = _rng(seed, _META)
     if name == "tiny":
