@@ -17,8 +17,12 @@ reads them, and nothing of one step is left for the next.
 
 Printed: one JSON line (metric, value = verified tokens/s per layer call,
 per-kernel times, achieved HBM bandwidth against the 8 TB/s peak, the same
-step in the deferred flow, and the CPU oracle's rate on a bounded sample of
-the same workload).
+step in the deferred flow, the stock speculative step on the same batch, the
+CPU oracle's rate on a bounded sample of the same workload). The default run
+adds sub-records of the other workloads ("workloads": the decode batch with
+the bounded gate, the deep-draft batch, the ragged batch, the 8-layer
+deferred workload) and the oracle's rate on samples of the tiny, ragged and
+deferred workloads.
 """
 
 from __future__ import annotations
@@ -82,7 +86,8 @@ def kernel_key(name: str) -> str:
     """Library kernel -> call name (by template mode); others keep their name."""
     if "kda_kernel<1," in name:
         return "kda_verify"
-    for mode, call in (("0", "kda_recurrent"), ("2", "kda_commit"), ("3", "kda_verify_deferred")):
+    for mode, call in (("0", "kda_recurrent"), ("2", "kda_commit"), ("3", "kda_verify_deferred"),
+                       ("4", "kda_recurrent_spec")):
         if f"kda_kernel<{mode}," in name:
             return call
     for mode, call in (("2", "kda_commit_layers"), ("3", "kda_flush_layers")):
@@ -159,18 +164,30 @@ def measured_traffic(kernel: str, workload: str):
     return None if k is None else k["traffic_bytes"]
 
 
+SUB_WORKLOADS = ("decode_bounded", "deep", "ragged", "deferred")
+METRIC = "KDA verify+commit tokens/s and achieved HBM GB/s vs peak (B=64,H=32,T=4)"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "deep", "ragged", "deferred"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "decode_bounded", "deep", "ragged", "deferred"],
+                    help="the workload of the headline line (the default line is the decode "
+                         "batch, with the other workloads as sub-records)")
     ap.add_argument("--sets", type=int, default=12,
                     help="layers per step, each with its own pool, inputs and records")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the CPU oracle sample")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="headline workload only: no sub-records of the other workloads")
+    ap.add_argument("--sub-steps", type=int, default=20, help="timed steps of each sub-record")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the decode CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="repeat the CPU sample until this much wall time is spent")
+                    help="repeat the decode CPU sample until this much wall time is spent")
+    ap.add_argument("--cpu-seconds-other", type=float, default=4.0,
+                    help="the same for the CPU samples of the other workloads")
     ap.add_argument("--align", action="store_true",
                     help="commit in align mode: a block table sends each row's state to other "
                          "blocks of the pool (decode/deep/ragged workloads)")
@@ -199,14 +216,91 @@ def main():
 
     import torch
     import linear_attention_speculative_kda_amd as kda
-    from workloads import make_batch
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload == "deferred":
         print(json.dumps(deferred_leg(args, torch, kda, dev)), flush=True)
         return
-    batch = make_batch(args.workload)
+    leg = serving_leg(args, torch, kda, dev, args.workload, args.sets, args.steps, args.warmup,
+                      headline=True)
+    stream = torch.cuda.current_stream()
+    copy_gbs = device_copy_gbs(torch, stream)
+    dom = leg["dominant"]
+    kernels = leg["kernels"]
+    result = {
+        "metric": METRIC,
+        "value": leg["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": leg["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": leg["config"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": kernels[dom]["gbs"],
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": kernels[dom]["gbs"] / PEAK_HBM_GBS,
+            "traffic": kernels[dom]["traffic"],
+        },
+    }
+    for key in ("kernels", "ms_per_layer_step", "step_gbs", "step_frac_of_peak", "step_timing",
+                "ms_per_step_eager", "value_eager", "commit_tokens_per_s", "verify_tokens_per_s",
+                "interleaved", "deferred_flow", "stock_spec"):
+        if key in leg:
+            result[key] = leg[key]
+    result["copy_gbs_measured"] = copy_gbs
+
+    if not args.no_sub and args.workload == "decode" and not args.align and not args.per_layer_commit:
+        subs = {}
+        for name in SUB_WORKLOADS:
+            sargs = argparse.Namespace(**vars(args))
+            sargs.steps = args.sub_steps
+            sargs.warmup = min(args.warmup, 5)
+            if name == "deferred":
+                d = deferred_leg(sargs, torch, kda, dev)
+                subs[name] = {k: d[k] for k in ("config", "roofline", "flows", "deferred_speedup",
+                                                "kda_conv_compact", "value", "ms_per_step")}
+                subs[name]["value_unit"] = "tokens/s (every layer's verified tokens per second)"
+            else:
+                sub = serving_leg(sargs, torch, kda, dev, name, args.sets, sargs.steps,
+                                  sargs.warmup)
+                subs[name] = {k: sub[k] for k in ("config", "value", "ms_per_layer_step", "step_gbs",
+                                                  "step_frac_of_peak", "kernels",
+                                                  "verify_tokens_per_s", "commit_tokens_per_s")}
+            print(f"sub-record {name} done", file=sys.stderr, flush=True)
+        result["workloads"] = subs
+
+    if not args.no_cpu:
+        batch = make_batch_for(args.workload)
+        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_rows, args.cpu_seconds)
+        if not args.no_sub and args.workload == "decode":
+            result["cpu_baselines_other"] = cpu_baselines_other(args.cpu_seconds_other)
+
+    print(json.dumps(result), flush=True)
+
+
+def make_batch_for(name):
+    from workloads import make_batch
+    return make_batch(name)
+
+
+def serving_leg(args, torch, kda, dev, name, L, K, W, headline=False):
+    """One workload's decode step in serving order over L layers: every
+    layer's kda_verify (the forward pass), then every layer's commit in one
+    kda_commit_layers launch (after sampling). Per-kernel times from HIP
+    events around eager launches; the step from a HIP graph of the whole
+    step replayed K times. headline: also the interleaved order, the
+    deferred flow and the stock speculative step on the same inputs."""
+    batch = make_batch_for(name)
     B, H, Q = batch.num_rows, batch.H, batch.Q
     T = batch.seq_lens()
     ntok = batch.tokens.num_tokens
@@ -239,7 +333,7 @@ def main():
 
     # ---- one input set per layer: pool, activations, records, outputs
     sets = []
-    for _ in range(args.sets):
+    for _ in range(L):
         qkv = up_bf16(batch.tokens.qkv)
         sets.append(dict(
             pool=pool0.clone(),
@@ -255,10 +349,9 @@ def main():
     # Each input set stands for one layer of the model: a step is the
     # serving order of one decode step, every layer's kda_verify (the forward
     # pass), then every layer's commit in one kda_commit_layers launch (after
-    # sampling). With 12 sets the step touches 12 x 128 MiB of checkpoints:
-    # the 256 MB MALL can carry at most the last two layers' checkpoints
-    # from their verify to the commit.
-    L = len(sets)
+    # sampling). With 12 sets the decode step touches 12 x 128 MiB of
+    # checkpoints: the 256 MB MALL can carry at most the last two layers'
+    # checkpoints from their verify to the commit.
     pools = [s["pool"] for s in sets]
     recs = [s["rec"] for s in sets]
 
@@ -305,12 +398,11 @@ def main():
         if ev is not None:
             ev[L + 1].record(st)
 
-    for _ in range(max(1, args.warmup // L)):
+    for _ in range(max(1, W // L)):
         step(stream)
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, events around every launch on the launch stream
-    K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 2)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -337,14 +429,19 @@ def main():
     commit_name = "kda_commit" if args.per_layer_commit and align is None else "kda_commit_layers"
     c_launch_bytes = cbytes * L / commit_launches
     c_launch_ms = c_ms / commit_launches
+    # the counter runs used the default step (12 layers, in-place commit in
+    # one launch); other shapes of the commit move other bytes
+    default_shape = L == 12 and align is None and not args.per_layer_commit
     kernels = {
         "kda_verify": dict(launches_per_step=L, avg_us=v_ms * 1e3,
                            median_us=float(np.median(tv)) * 1e3, bytes=vbytes,
-                           gbs=vbytes / (v_ms * 1e6), tokens_per_s=tok_verify / (v_ms * 1e-3)),
+                           gbs=vbytes / (v_ms * 1e6), tokens_per_s=tok_verify / (v_ms * 1e-3),
+                           traffic=measured_traffic("kda_verify", name)),
         commit_name: dict(launches_per_step=commit_launches, layers_per_launch=L // commit_launches,
                           avg_us=c_launch_ms * 1e3, median_us=float(np.median(tc)) / commit_launches * 1e3,
                           bytes=c_launch_bytes, gbs=c_launch_bytes / (c_launch_ms * 1e6),
-                          tokens_per_s=tok_commit * L / (c_ms * 1e-3)),
+                          tokens_per_s=tok_commit * L / (c_ms * 1e-3),
+                          traffic=measured_traffic(commit_name, name) if default_shape else None),
     }
     for kinfo in kernels.values():
         kinfo["frac_of_peak"] = kinfo["gbs"] / PEAK_HBM_GBS
@@ -363,7 +460,7 @@ def main():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step(torch.cuda.current_stream())
-    for _ in range(max(1, args.warmup // L)):
+    for _ in range(max(1, W // L)):
         graph.replay()
     torch.cuda.synchronize()
     g_start = torch.cuda.Event(enable_timing=True)
@@ -375,11 +472,58 @@ def main():
     torch.cuda.synchronize()
     ms_step_graph = g_start.elapsed_time(g_end) / K
     ms_layer = ms_step_graph / L
+    del graph
 
-    # ---- context: one layer's verify then its own commit, back to back
-    # (kda_commit per layer). The commit then re-reads the checkpoints the
-    # verify has just read, partly from the MALL, and the next verify streams
-    # its checkpoints while that commit's new state is written back to HBM.
+    step_bytes = L * (vbytes + cbytes)
+    tshape = "ragged 1..8" if name == "ragged" else int(T.max())
+    out = {
+        "value": L * tok_verify / (ms_step_graph * 1e-3),
+        "ms_per_step": ms_step_graph,
+        "config": {
+            "workload": f"{batch.name}: B={B} H={H} K=V=128 T={tshape} Q={Q}, bf16 activations, fp32 "
+                        f"checkpoints, {'bounded gate lb=' + str(batch.lower_bound) if batch.lower_bound is not None else 'unbounded gate'}; "
+                        f"a step = {L} layers (own pool, inputs and records each): every layer's "
+                        f"kda_verify, then "
+                        f"{'one kda_commit per layer' if args.per_layer_commit else 'one kda_commit_layers for all layers'}; "
+                        f"value = verified tokens per second per layer call",
+            "B": B, "H": H, "K": 128, "V": 128, "T": tshape, "window": Q, "layers_per_step": L,
+            "max_seqlen": max_seqlen,
+            "verified_tokens_per_layer": tok_verify, "committed_tokens_per_layer": tok_commit,
+            "commit": "align mode (block table, destinations other than the sources)" if args.align
+                      else "in place",
+        },
+        "dominant": dom,
+        "kernels": kernels,
+        "ms_per_layer_step": ms_layer,
+        "step_gbs": step_bytes / (ms_step_graph * 1e6),
+        "step_frac_of_peak": step_bytes / (ms_step_graph * 1e6) / PEAK_HBM_GBS,
+        "step_timing": "HIP graph replay of whole steps; per-kernel times from HIP events around "
+                       "eager launches",
+        "ms_per_step_eager": ms_step,
+        "value_eager": L * tok_verify / (ms_step * 1e-3),
+        "commit_tokens_per_s": tok_commit * L / (c_ms * 1e-3),
+        "verify_tokens_per_s": tok_verify / (v_ms * 1e-3),
+    }
+    if headline:
+        out["interleaved"] = interleaved_leg(torch, sets, verify, commit_one, stream, K, L,
+                                             tok_verify, vbytes + cbytes)
+        if align is None:
+            out["deferred_flow"] = decode_deferred_flow(
+                args, torch, kda, layer, sets, cu, si, nacc, stream, T, n_commit, valid, H, B, Q,
+                dev, tok_verify)
+            out["stock_spec"] = stock_spec_leg(torch, kda, dev, batch, layer, sets, cu, stream, K,
+                                               W, L, (L * v_ms + c_ms) / L, vbytes + cbytes)
+    del sets, pools, recs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def interleaved_leg(torch, sets, verify, commit_one, stream, K, L, tok_verify, layer_bytes):
+    """Context: one layer's verify then its own commit, back to back
+    (kda_commit per layer). The commit then re-reads the checkpoints the
+    verify has just read, partly from the MALL, and the next verify streams
+    its checkpoints while that commit's new state is written back to HBM."""
     Ki = max(4, min(K, 60))
     evi = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(Ki)]
     for i in range(L):
@@ -400,81 +544,83 @@ def main():
     ti_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evi]))
     ti_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evi]))
     ms_inter = a0.elapsed_time(a1) / Ki
-    interleaved = {
+    return {
         "ms_per_layer_step": ms_inter,
         "value": tok_verify / (ms_inter * 1e-3),
         "kda_verify_avg_us": ti_v * 1e3,
         "kda_commit_avg_us": ti_c * 1e3,
-        "gbs": (vbytes + cbytes) / (ms_inter * 1e6),
+        "gbs": layer_bytes / (ms_inter * 1e6),
         "note": "each layer's verify followed at once by its own single-layer commit (eager "
                 "launches); not the serving order",
     }
 
-    deferred = None if align is not None else decode_deferred_flow(
-        args, torch, kda, layer, sets, cu, si, nacc, stream, T, n_commit, valid, H, B, Q, dev,
-        tok_verify)
 
-    copy_gbs = device_copy_gbs(torch, stream)
+def spec_bytes(T, cols, valid, H):
+    """Bytes of the stock speculative step (each counted once): per valid
+    (row, head) the source state read, one state written per token in a
+    column, each token's inputs and its output:
+    65,536 (1 + min(T_i, cols)) + 1,282 T_i."""
+    T = np.asarray(T)[valid]
+    return float(H * np.sum(STATE_BYTES * (1 + np.minimum(T, cols)) + (TOKEN_IN_BYTES + OUT_BYTES) * T))
 
-    step_bytes = L * (vbytes + cbytes)
-    result = {
-        "metric": "KDA verify+commit tokens/s and achieved HBM GB/s vs peak (B=64,H=32,T=4)",
-        "value": L * tok_verify / (ms_step_graph * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step_graph,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp32",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{batch.name}: B={B} H={H} K=V=128 T={'ragged' if batch.name == 'ragged' else int(T.max())} "
-                        f"Q={Q}, bf16 activations, fp32 checkpoints; a step = {L} layers (own pool, "
-                        f"inputs and records each): every layer's kda_verify, then "
-                        f"{'one kda_commit per layer' if args.per_layer_commit else 'one kda_commit_layers for all layers'}; "
-                        f"value = verified tokens per second per layer call",
-            "B": B, "H": H, "K": 128, "V": 128, "T": int(T.max()), "window": Q, "layers_per_step": L,
-            "max_seqlen": max_seqlen,
-            "verified_tokens_per_layer": tok_verify, "committed_tokens_per_layer": tok_commit,
-            "commit": "align mode (block table, destinations other than the sources)" if args.align
-                      else "in place",
-        },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": dom,
-            "achieved": kernels[dom]["gbs"],
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": kernels[dom]["gbs"] / PEAK_HBM_GBS,
-            # the counter runs used the default step (12 layers, in-place
-            # commit in one launch); other shapes of the commit move other bytes
-            "traffic": measured_traffic(dom, args.workload)
-                       if dom == "kda_verify" or (L == 12 and align is None and not args.per_layer_commit)
-                       else None,
-        },
-        "kernels": kernels,
-        "ms_per_layer_step": ms_layer,
-        "step_gbs": step_bytes / (ms_step_graph * 1e6),
-        "step_frac_of_peak": step_bytes / (ms_step_graph * 1e6) / PEAK_HBM_GBS,
-        "step_timing": "HIP graph replay of whole steps; per-kernel times from HIP events around "
-                       "eager launches",
-        "ms_per_step_eager": ms_step,
-        "value_eager": L * tok_verify / (ms_step * 1e-3),
-        "commit_tokens_per_s": tok_commit * L / (c_ms * 1e-3),
-        "verify_tokens_per_s": tok_verify / (v_ms * 1e-3),
-        "interleaved": interleaved,
-        "copy_gbs_measured": copy_gbs,
+
+def stock_spec_leg(torch, kda, dev, batch, layer, sets, cu, stream, K, W, L, recover_ms_per_layer,
+                   recover_bytes_per_layer):
+    """The stock speculative step that RecoverSSM replaces, on the same
+    activations: per layer one kda_recurrent_spec over 1 + num_spec columns
+    of distinct blocks per request (its own pool per layer), which stores
+    one full state per verified token. The source column of a row is its
+    accepted count of the previous step minus one (the workload's counts,
+    clamped to 1..cols). Events around every launch, K steps of L layers."""
+    B, H = batch.num_rows, batch.H
+    T = batch.seq_lens()
+    cols = int(T.max())
+    nslots = 1 + B * cols
+    table = torch.arange(1, nslots, dtype=torch.int32, device=dev).view(B, cols)
+    acc = torch.from_numpy(np.clip(batch.num_accepted, 1, cols).astype(np.int32)).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    pools = []
+    for _ in range(L):
+        pool = torch.empty((nslots, H, 128, 128), dtype=torch.float32, device=dev)
+        pool.normal_(0.0, 0.02, generator=gen)
+        pools.append(pool)
+
+    def run(i, st):
+        s = sets[i]
+        kda.kda_recurrent_spec(layer, s["q"], s["k"], s["v"], s["g"], s["beta"], cu, pools[i], table,
+                               acc, s["o"], stream=st)
+
+    for _ in range(max(1, W // L)):
+        for i in range(L):
+            run(i, stream)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(L)] for _ in range(K)]
+    for k in range(K):
+        for i in range(L):
+            ev[k][i][0].record(stream)
+            run(i, stream)
+            ev[k][i][1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for row in ev for a, b in row])
+    valid = batch.valid_rows()
+    nbytes = spec_bytes(T, cols, valid, H)
+    us = float(t.mean()) * 1e3
+    del pools
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {
+        "kda_recurrent_spec": dict(avg_us=us, median_us=float(np.median(t)) * 1e3, bytes=nbytes,
+                                   gbs=nbytes / (us * 1e3), frac_of_peak=nbytes / (us * 1e3) / PEAK_HBM_GBS,
+                                   columns=cols),
+        "bytes_vs_verify_commit": nbytes / recover_bytes_per_layer,
+        "time_vs_verify_commit": (us * 1e-3) / recover_ms_per_layer,
+        "verify_commit_ms_per_layer": recover_ms_per_layer,
+        "verify_commit_bytes_per_layer": recover_bytes_per_layer,
+        "note": "per layer: the stock step (one state stored per verified token) against "
+                "RecoverSSM's verify + commit on the same batch (their event times per layer)",
     }
-    if deferred is not None:
-        result["deferred_flow"] = deferred
-
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_rows, args.cpu_seconds)
-
-    print(json.dumps(result), flush=True)
 
 
 def decode_deferred_flow(args, torch, kda, layer, sets, cu, si, nacc, stream, T, n_commit, valid,
@@ -795,6 +941,58 @@ def deferred_leg(args, torch, kda, dev):
                              "bytes": conv_bytes, "gbs": conv_bytes / (conv_us * 1e3)},
         "copy_gbs_measured": copy_gbs,
     }
+
+
+def cpu_baselines_other(seconds):
+    """The oracle on bounded samples of the other workloads, one thread each:
+    the tiny batch whole, 32 of the ragged batch's 128 rows, and the
+    deferred workload's sequential replay (layer 0, 16 of 512 requests, all
+    4 steps: each step's verify, then the commit of the accepted prefix)."""
+    from workloads import make_batch
+    out = {"tiny": cpu_baseline(make_batch("tiny"), 4, seconds),
+           "ragged": cpu_baseline(make_batch("ragged"), 32, seconds),
+           "deferred": cpu_replay_deferred(16, seconds)}
+    return out
+
+
+def cpu_replay_deferred(rows, seconds):
+    from threadpoolctl import threadpool_limits
+    from oracle import kda_ref as ref
+    from workloads import make_deferred
+    run = make_deferred()
+    B, H, Q, K = run.B, run.H, run.Q, 128
+    p = run.params[0]
+    lay = ref.Layer(p.a_log, p.g_bias, run.scale, run.lower_bound)
+    # a compact pool: the sampled requests' checkpoints in slots 1..rows
+    si = np.zeros(B, np.int32)
+    si[:rows] = np.arange(1, rows + 1)
+    pool0 = np.zeros((rows + 1, H, K, K), np.float32)
+    for i in range(rows):
+        pool0[i + 1] = run.slot_state(0, int(run.state_indices[i]))
+    toks = [run.tokens(0, s) for s in range(run.steps)]
+    accs = [run.num_accepted(s) for s in range(run.steps)]
+    ntok = B * run.T
+    n_tok = rows * run.T * run.steps
+    walls = []
+    with threadpool_limits(1):
+        while sum(walls) < seconds or len(walls) < 1:
+            pool = pool0.copy()
+            t0 = time.perf_counter()
+            for s in range(run.steps):
+                t = toks[s]
+                rec = ref.Records.empty(B, H, Q, K)
+                o = np.zeros((ntok, H, K), np.uint16)
+                ref.kda_verify(lay, t.q, t.k, t.v, t.g, t.beta, run.cu_seqlens, pool, si, rec, o,
+                               record_rows=run.record_rows)
+                ref.kda_commit(lay, run.cu_seqlens, ntok, pool, si, rec, accs[s],
+                               record_rows=run.record_rows)
+            walls.append(time.perf_counter() - t0)
+    wall = float(np.median(walls))
+    return {"value": n_tok / wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequential replay of layer 0 for {rows} of {B} requests over {run.steps} "
+                      f"steps ({n_tok} tokens, all {H} heads; each step's verify then commit), "
+                      f"NumPy fp64 on one thread, median of {len(walls)} runs ({wall:.2f} s each)",
+            "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline(batch, rows, seconds):
