@@ -242,13 +242,19 @@ __device__ __forceinline__ float reduce8(float x) {
   return x;
 }
 
-// Sum over the 32 lanes of a half-wave; every lane gets the same bits.
+// Sum over the 32 lanes of a half-wave; every lane gets the same bits. The
+// two 16-lane rows of each half-wave are summed in their lanes (DPP), then
+// added as scalars read from the rows' first lanes (no LDS round trip: a
+// ds_swizzle across the rows waited behind the workgroup's other LDS
+// traffic). Either half of the wave adds the same two row sums.
 __device__ __forceinline__ float reduce32(float x) {
   x = reduce8(x);
   x = x + dpp<0x140>(x);  // row_mirror: lane i <-> 15-i (the other 8-group)
-  // ds_swizzle bit mode, xor 16: lane j reads lane j ^ 16 (the other row)
-  x = x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (16 << 10) | 0x1F));
-  return x;
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
 }
 
 __device__ __forceinline__ void unpack4(uint2 raw, float out[4]) {
@@ -589,10 +595,10 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
 // q^, exp(g), by 256 threads (c.tid 0..255; c.hw and c.l32 relative to them).
 template <int BV, int TMAX, int NT>
 __device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c, int T) {
-  // Decayed vectors: threads 0..127, one key channel each (all of the
+  // Decayed vectors: threads 128..255, one key channel each (all of the
   // channel's staged values are read first, then a short product chain).
-  if (c.tid < KD) {
-    const int ch = c.tid;
+  if (c.tid >= KD) {
+    const int ch = c.tid - KD;
     float kk[TMAX], qq[TMAX], dd[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
@@ -614,49 +620,65 @@ __device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c,
     st.av[2 * NT][ch] = 0.0f;
   }
   // Coefficients: the T(T+1)/2 pairs (s, t), s <= t, numbered t(t+1)/2 + s,
-  // are dealt to the 8 half-waves; each lane covers 4 key channels. The pair
-  // is chosen by the half-wave's data (LDS addresses), not by branching, so
-  // both halves of a wave run the same instructions.
+  // dealt to the 16 rows of 16 lanes (pair q to row q % 16; a 4-token chunk
+  // takes one pass of rows 0..9, an 8-token chunk three passes); lane j of a
+  // row covers the key channels 4j..4j+3 and 64+4j..64+4j+3, and the row
+  // sums with 4 DPP steps. Every chunk size computes a pair with the same
+  // operations, so the chunk size does not change the bits.
   {
-    const int l = c.l32;
-    float4 dk4[TMAX];
-#pragma unroll
-    for (int r = 0; r < TMAX; ++r)
-      dk4[r] = (r < T) ? *reinterpret_cast<const float4*>(&st.dk[r][4 * l]) : make_float4(1.f, 1.f, 1.f, 1.f);
+    const int r16 = c.tid >> 4, j = c.tid & 15;
     const int npairs = T * (T + 1) / 2;
-    constexpr int kSlots = (TMAX * (TMAX + 1) / 2 + 7) / 8;
+    constexpr int kSlots = (TMAX * (TMAX + 1) / 2 + 15) / 16;
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j) {
-      const int q = c.hw + 8 * j;
-      const bool live = q < npairs;
-      // pair number q -> (s, t): t is the largest with t(t+1)/2 <= q
-      int t = 0;
+    for (int slot = 0; slot < kSlots; ++slot) {
+      const int q = r16 + 16 * slot;
+      if (q < TMAX * (TMAX + 1) / 2) {
+        const bool live = q < npairs;
+        // pair number q -> (s, t): t is the largest with t(t+1)/2 <= q
+        int t = 0;
 #pragma unroll
-      for (int u = 1; u < TMAX; ++u) t += (u * (u + 1) / 2 <= q) ? 1 : 0;
-      const int sidx = live ? q - t * (t + 1) / 2 : 0;
-      const int tidx = live ? t : 0;
-      float4 w = *reinterpret_cast<const float4*>(&st.kh[sidx][4 * l]);
+        for (int u = 1; u < TMAX; ++u) t += (u * (u + 1) / 2 <= q) ? 1 : 0;
+        const int sidx = live ? q - t * (t + 1) / 2 : 0;
+        const int tidx = live ? t : 0;
+        float4 wa = *reinterpret_cast<const float4*>(&st.kh[sidx][4 * j]);
+        float4 wb = *reinterpret_cast<const float4*>(&st.kh[sidx][64 + 4 * j]);
 #pragma unroll
-      for (int r = 1; r < TMAX; ++r) {
-        if (r > sidx && r <= tidx) {
-          w.x *= dk4[r].x; w.y *= dk4[r].y; w.z *= dk4[r].z; w.w *= dk4[r].w;
+        for (int r = 1; r < TMAX; ++r) {
+          if (r > sidx && r <= tidx) {
+            const float4 da = *reinterpret_cast<const float4*>(&st.dk[r][4 * j]);
+            const float4 db = *reinterpret_cast<const float4*>(&st.dk[r][64 + 4 * j]);
+            wa.x *= da.x; wa.y *= da.y; wa.z *= da.z; wa.w *= da.w;
+            wb.x *= db.x; wb.y *= db.y; wb.z *= db.z; wb.w *= db.w;
+          }
         }
-      }
-      const float4 x = *reinterpret_cast<const float4*>(&st.qh[tidx][4 * l]);
-      const float4 y = *reinterpret_cast<const float4*>(&st.kh[tidx][4 * l]);
-      float nts = w.x * x.x;
-      nts = fmaf(w.y, x.y, nts);
-      nts = fmaf(w.z, x.z, nts);
-      nts = fmaf(w.w, x.w, nts);
-      float mts = w.x * y.x;
-      mts = fmaf(w.y, y.y, mts);
-      mts = fmaf(w.z, y.z, mts);
-      mts = fmaf(w.w, y.w, mts);
-      nts = reduce32(nts);
-      mts = reduce32(mts);
-      if (live && l == 0) {
-        st.N[tidx][sidx] = nts;
-        st.M[tidx][sidx] = sidx < tidx ? mts : 0.0f;
+        const float4 xa = *reinterpret_cast<const float4*>(&st.qh[tidx][4 * j]);
+        const float4 xb = *reinterpret_cast<const float4*>(&st.qh[tidx][64 + 4 * j]);
+        const float4 ya = *reinterpret_cast<const float4*>(&st.kh[tidx][4 * j]);
+        const float4 yb = *reinterpret_cast<const float4*>(&st.kh[tidx][64 + 4 * j]);
+        float nts = wa.x * xa.x;
+        nts = fmaf(wa.y, xa.y, nts);
+        nts = fmaf(wa.z, xa.z, nts);
+        nts = fmaf(wa.w, xa.w, nts);
+        nts = fmaf(wb.x, xb.x, nts);
+        nts = fmaf(wb.y, xb.y, nts);
+        nts = fmaf(wb.z, xb.z, nts);
+        nts = fmaf(wb.w, xb.w, nts);
+        float mts = wa.x * ya.x;
+        mts = fmaf(wa.y, ya.y, mts);
+        mts = fmaf(wa.z, ya.z, mts);
+        mts = fmaf(wa.w, ya.w, mts);
+        mts = fmaf(wb.x, yb.x, mts);
+        mts = fmaf(wb.y, yb.y, mts);
+        mts = fmaf(wb.z, yb.z, mts);
+        mts = fmaf(wb.w, yb.w, mts);
+        nts = reduce8(nts);
+        mts = reduce8(mts);
+        nts = nts + dpp<0x140>(nts);   // row_mirror: the other 8 lanes of the row
+        mts = mts + dpp<0x140>(mts);
+        if (live && j == 0) {
+          st.N[tidx][sidx] = nts;
+          st.M[tidx][sidx] = sidx < tidx ? mts : 0.0f;
+        }
       }
     }
   }
@@ -888,11 +910,10 @@ __device__ __forceinline__ void chunk_verify_mfma(const float (&S)[R][16], Stage
 
 // A chunk that fits the window: the matrix-core form where the tile allows
 // it, else the vector form.
-template <int R, int BV, int TMAX, int NT>
-__device__ __forceinline__ void chunk_verify_one(float (&S)[R][16], StageChunk<BV, NT>& st,
+template <int R, int BV, int TMAX, int NT, class XB>
+__device__ __forceinline__ void chunk_verify_one(float (&S)[R][16], StageChunk<BV, NT>& st, XB& xb,
                                                  const Params& p, const Ctx& c, int T, long long tok0) {
   if constexpr (R >= 2) {
-    __shared__ XBuf<R> xb;
     chunk_verify_mfma<R, BV, TMAX, NT>(S, st, xb, p, c, T, tok0);
   } else {
     chunk_verify<R, BV, TMAX, NT>(S, st, p, c, T, tok0);
@@ -967,11 +988,16 @@ template <int MODE, int R, int TMAX, bool SHORT = false>
 __device__ __forceinline__ void kda_block(const Params& p, int b) {
   constexpr int BV = R * NWAVES * 8;   // value rows per workgroup
   constexpr bool kChunk = (MODE == kVerify || MODE == kDeferred);
-  // tokens staged at a time: the verify stages one chunk of its window
-  // (TMAX); the replays of the other modes stage up to CH records or tokens
-  constexpr int SNT = MODE == kVerify ? TMAX : CH;
+  // tokens staged at a time: the verify modes stage one chunk of a window
+  // (TMAX) and replay records in chunks of the same size; the other modes
+  // stage up to CH records or tokens
+  constexpr int SNT = kChunk ? TMAX : CH;
   using StageT = typename std::conditional<kChunk, StageChunk<BV, SNT>, Stage<BV, SNT>>::type;
   __shared__ StageT st;
+  // the matrix-core verify's per-wave LDS
+  struct NoXBuf {};
+  using XBufT = typename std::conditional<(kChunk && R >= 2), XBuf<R>, NoXBuf>::type;
+  __shared__ XBufT xbuf;
 
   Ctx c;
   c.tid = threadIdx.x;
@@ -1069,7 +1095,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
       __builtin_amdgcn_sched_barrier(0);
       stage_compute<MODE, BV, SNT>(st, raw, p, c, false, 0, false);
       lds_barrier();
-      chunk_verify_one<R, BV, TMAX, SNT>(S, st, p, c, nmain, (long long)bos);
+      chunk_verify_one<R, BV, TMAX, SNT>(S, st, xbuf, p, c, nmain, (long long)bos);
       // the records last: stores issued behind the state loads would make
       // later register reuse wait for those loads
       store_records<BV>(raw, p, c, 0);
@@ -1087,7 +1113,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   // registers by the time the folded state has been stored, and no load
   // issued behind that store waits for its write.
   if constexpr (MODE == kDeferred) {
-    if (chunk && nfold <= CH) {
+    if (chunk && nfold <= SNT) {
       Raw<BV> rf, rv;
       stage_load<MODE, BV>(rf, p, c, true, 0, nfold);
       stage_load<MODE, BV>(rv, p, c, false, 0, nmain);
@@ -1103,7 +1129,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
         lds_barrier();   // the fold's staged tokens are consumed
         stage_compute<MODE, BV, SNT>(st, rv, p, c, false, 0, false);
         lds_barrier();
-        chunk_verify_one<R, BV, TMAX, SNT>(S, st, p, c, nmain, (long long)bos);
+        chunk_verify_one<R, BV, TMAX, SNT>(S, st, xbuf, p, c, nmain, (long long)bos);
         store_records<BV>(rv, p, c, 0);
       }
       return;
