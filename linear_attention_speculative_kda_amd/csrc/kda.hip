@@ -620,8 +620,8 @@ __device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c,
     st.av[2 * NT][ch] = 0.0f;
   }
   // Coefficients: the T(T+1)/2 pairs (s, t), s <= t, numbered t(t+1)/2 + s,
-  // dealt to the 16 rows of 16 lanes (pair q to row q % 16; a 4-token chunk
-  // takes one pass of rows 0..9, an 8-token chunk three passes); lane j of a
+  // dealt to the 16 rows of 16 lanes (pair q to row q % 16; one pass for up
+  // to 5 tokens, two for 6 or 7, three for 8); lane j of a
   // row covers the key channels 4j..4j+3 and 64+4j..64+4j+3, and the row
   // sums with 4 DPP steps. Every chunk size computes a pair with the same
   // operations, so the chunk size does not change the bits.
@@ -632,7 +632,8 @@ __device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c,
 #pragma unroll
     for (int slot = 0; slot < kSlots; ++slot) {
       const int q = r16 + 16 * slot;
-      if (q < TMAX * (TMAX + 1) / 2) {
+      // (a pass with no live pair is skipped: the test is uniform)
+      if (16 * slot < npairs && q < TMAX * (TMAX + 1) / 2) {
         const bool live = q < npairs;
         // pair number q -> (s, t): t is the largest with t(t+1)/2 <= q
         int t = 0;
