@@ -192,7 +192,8 @@ typedef struct kda_conv_state {
  * Errors: NULL -> KDA_ERR_NULL; head_dim != 128 -> KDA_ERR_UNSUPPORTED;
  * H <= 0, negative sizes or strides too small -> KDA_ERR_SHAPE; misaligned
  * (state 16 B, q/k/v/g 8 B with token strides multiple of 4) -> KDA_ERR_ALIGN;
- * o overlapping the pool or a token array -> KDA_ERR_ALIAS.
+ * o overlapping the pool or a token array, or a token array overlapping the
+ * pool (which is written) -> KDA_ERR_ALIAS.
  */
 kda_status kda_recurrent(const kda_layer* layer, const kda_tokens* tokens,
                          const kda_pool* pool, uint16_t* o, hipStream_t stream);
@@ -220,7 +221,8 @@ kda_status kda_recurrent(const kda_layer* layer, const kda_tokens* tokens,
  *   o: [num_tokens, H, 128] bf16.
  * Blocks named by one row must not be named by another row. Errors as
  * kda_recurrent, plus: table NULL -> KDA_ERR_NULL; cols < 1 or
- * row_stride < cols -> KDA_ERR_SHAPE.
+ * row_stride < cols -> KDA_ERR_SHAPE; the block ids or the counts
+ * overlapping the pool or o -> KDA_ERR_ALIAS.
  */
 kda_status kda_recurrent_spec(const kda_layer* layer, const kda_tokens* tokens,
                               const kda_pool* pool, const kda_spec_table* table,

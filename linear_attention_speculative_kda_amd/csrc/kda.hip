@@ -1863,7 +1863,9 @@ kda_status kda_recurrent(const kda_layer* layer, const kda_tokens* tokens, const
   if (!aligned(o, 2)) return KDA_ERR_ALIGN;
   Ranges in;
   token_ranges(tokens, H, in);
-  in.add(pool_range(pool, H));
+  const Range prange = pool_range(pool, H);
+  if (any_overlap(prange, in)) return KDA_ERR_ALIAS;   // the pool is written
+  in.add(prange);
   const Range orange = range_of(o, (long long)tokens->num_tokens * H * KD * 2);
   if (any_overlap(orange, in)) return KDA_ERR_ALIAS;
   Params p = base_params(layer);
@@ -1889,9 +1891,18 @@ kda_status kda_recurrent_spec(const kda_layer* layer, const kda_tokens* tokens, 
   if (!aligned(o, 2)) return KDA_ERR_ALIGN;
   Ranges in;
   token_ranges(tokens, H, in);
-  in.add(pool_range(pool, H));
+  const Range prange = pool_range(pool, H);
+  if (any_overlap(prange, in)) return KDA_ERR_ALIAS;   // the pool is written
+  in.add(prange);
   const Range orange = range_of(o, (long long)tokens->num_tokens * H * KD * 2);
   if (any_overlap(orange, in)) return KDA_ERR_ALIAS;
+  // the block ids and counts are read while the pool and o are written
+  const Range trange = range_of(table->indices,
+                                ((long long)(tokens->num_rows - 1) * table->row_stride + table->cols) * 4);
+  const Range arange = range_of(table->num_accepted, table->num_accepted ? (long long)tokens->num_rows * 4 : 0);
+  if (overlap(trange, prange) || overlap(trange, orange) || overlap(arange, prange) ||
+      overlap(arange, orange))
+    return KDA_ERR_ALIAS;
   Params p = base_params(layer);
   set_tokens(p, tokens);
   set_pool(p, pool);

@@ -154,9 +154,24 @@ def test_recurrent_spec_validation():
     assert spec(o=0) == E["KDA_ERR_NULL"]
     assert spec(o=A + 0x1000000 + 1024) == E["KDA_ERR_ALIAS"]     # o inside the pool
     assert spec(o=A + 0x100000 + 64) == E["KDA_ERR_ALIAS"]        # o inside the tokens
+    # the block ids or the counts inside the pool or o (both are written)
+    assert spec(tab=_lib.KdaSpecTable(indices=A + 0x1000000 + 4096, row_stride=4, cols=4,
+                                      num_accepted=A + 0x700000)) == E["KDA_ERR_ALIAS"]
+    assert spec(tab=_lib.KdaSpecTable(indices=A + 0x600000, row_stride=4, cols=4,
+                                      num_accepted=O + 16)) == E["KDA_ERR_ALIAS"]
+    # a token array inside the pool
+    assert spec(T=tokens(q=A + 0x1000000 + 8192)) == E["KDA_ERR_ALIAS"]
     # no rows: nothing to do, even without a table array
     assert spec(T=tokens(n_rows=0, num_tokens=0),
                 tab=_lib.KdaSpecTable(indices=0, row_stride=4, cols=4)) == E["KDA_OK"]
+
+
+def test_recurrent_alias():
+    lib = _lib.load()
+    rec = lambda T, o=O: lib.kda_recurrent(ctypes.byref(layer()), ctypes.byref(T),  # noqa: E731
+                                           ctypes.byref(pool()), o, None)
+    assert rec(tokens(), o=A + 0x1000000 + 1024) == E["KDA_ERR_ALIAS"]   # o inside the pool
+    assert rec(tokens(g=A + 0x1000000 + 8192)) == E["KDA_ERR_ALIAS"]     # g inside the pool
 
 
 def test_empty_batch_is_a_no_op():
