@@ -62,7 +62,7 @@
 namespace {
 
 constexpr int KD = 128;        // head dim (K == V)
-constexpr int NTHREADS = 256;  // 4 waves
+constexpr int NTHREADS = 256;  // 4 waves: every kernel but the 8-wave deferred verify
 constexpr int NWAVES = 4;
 constexpr int CH = 8;          // tokens staged in LDS per chunk
 constexpr int MAX_WINDOW = 64;
@@ -363,8 +363,10 @@ __device__ __forceinline__ void lds_row16(const float* vec, int p8, float out[16
   }
 }
 
+template <int R, int BV>
 __device__ __forceinline__ int row_in_tile(int rr, const Ctx& c) {
-  return (rr * NWAVES + c.wave) * 8 + c.grp;
+  constexpr int NW = BV / (8 * R);   // waves of the workgroup
+  return (rr * NW + c.wave) * 8 + c.grp;
 }
 
 // A 16-byte load of state; NT: non-temporal (streamed: the line is not kept
@@ -396,7 +398,7 @@ template <int R, int BV, bool NT = false>
 __device__ __forceinline__ void load_tile(float (&S)[R][16], const float* sbase, const Ctx& c) {
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
-    const float* src = sbase + (c.tile * BV + row_in_tile(rr, c)) * KD + c.p8 * 4;
+    const float* src = sbase + (c.tile * BV + row_in_tile<R, BV>(rr, c)) * KD + c.p8 * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float4 x = ld_state4<NT>(src + j * 32);
@@ -409,7 +411,7 @@ template <int R, int BV, bool NT = false>
 __device__ __forceinline__ void store_tile(const float (&S)[R][16], float* sbase, const Ctx& c) {
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
-    float* dst = sbase + (c.tile * BV + row_in_tile(rr, c)) * KD + c.p8 * 4;
+    float* dst = sbase + (c.tile * BV + row_in_tile<R, BV>(rr, c)) * KD + c.p8 * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (NT) {
@@ -555,7 +557,7 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
       for (int e = 0; e < 16; ++e) S[rr][e] = S[rr][e] * dk[e];
       // delta rule against the decayed state, then the rank-1 update
       const float kv = row_dot(S[rr], kh);
-      const float u = beta * (st.vt[t][row_in_tile(rr, c)] - kv);
+      const float u = beta * (st.vt[t][row_in_tile<R, BV>(rr, c)] - kv);
 #pragma unroll
       for (int e = 0; e < 16; ++e) S[rr][e] = fmaf(kh[e], u, S[rr][e]);
     }
@@ -566,7 +568,7 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
         const float ov = row_dot(S[rr], qh);
-        if (c.p8 == 0) orow[row_in_tile(rr, c)] = f32_to_bf16(ov);
+        if (c.p8 == 0) orow[row_in_tile<R, BV>(rr, c)] = f32_to_bf16(ov);
       }
     }
     if constexpr (SPEC) {
@@ -592,12 +594,13 @@ __device__ __forceinline__ void seq_tokens(float (&S)[R][16], const Stage<BV, NT
 // longer than one chunk run chunk after chunk (chunk_advance in between).
 //
 // coef_phase: the per-chunk vectors and coefficients, from the staged k^,
-// q^, exp(g), by 256 threads (c.tid 0..255; c.hw and c.l32 relative to them).
+// q^, exp(g), by threads 0..255 (c.hw and c.l32 relative to them; the
+// threads beyond them in an 8-wave workgroup take no part).
 template <int BV, int TMAX, int NT>
 __device__ __forceinline__ void coef_phase(StageChunk<BV, NT>& st, const Ctx& c, int T) {
   // Decayed vectors: threads 128..255, one key channel each (all of the
   // channel's staged values are read first, then a short product chain).
-  if (c.tid >= KD) {
+  if (c.tid >= KD && c.tid < 2 * KD) {
     const int ch = c.tid - KD;
     float kk[TMAX], qq[TMAX], dd[TMAX];
 #pragma unroll
@@ -715,7 +718,7 @@ __device__ __forceinline__ void chunk_recur(const StageChunk<BV, NT>& st, const 
                                             float (&u)[R][TMAX]) {
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
-    const int vloc = row_in_tile(rr, c);
+    const int vloc = row_in_tile<R, BV>(rr, c);
     float mine = 0.0f;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
@@ -801,15 +804,17 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // Per-wave LDS of the matrix-core path: the transpose buffer (16 rows x 32
 // keys), then, once the products are done, the regrouped a_t, b_t of the
 // wave's rows (20 floats per row: a_0..a_7, b_0..b_7, padding).
-template <int R>
+template <int R, int NW>
 struct XBuf {
   static constexpr int kFloats = (16 * 32 > 16 * (R / 2) * 20) ? 16 * 32 : 16 * (R / 2) * 20;
-  float w[NWAVES][kFloats];
+  float w[NW][kFloats];
 };
 
 // The tile row of MFMA row i of block blk (register sets 2 blk, 2 blk + 1).
+template <int R, int BV>
 __device__ __forceinline__ int xrow(int blk, int i, const Ctx& c) {
-  return ((2 * blk + (i >> 3)) * NWAVES + c.wave) * 8 + (i & 7);
+  constexpr int NW = BV / (8 * R);
+  return ((2 * blk + (i >> 3)) * NW + c.wave) * 8 + (i & 7);
 }
 
 template <int R, int BV, int NT>
@@ -871,7 +876,7 @@ __device__ __forceinline__ void xpose_recur(const floatx4 (&D)[R / 2], const Sta
   }
   if (lane >= 16 * (R / 2)) return;
   const int blk = lane >> 4, i = lane & 15;
-  const int vloc = xrow(blk, i, c);
+  const int vloc = xrow<R, BV>(blk, i, c);
   const float* rowd = xb + lane * 20;
   float a[TMAX], b[TMAX], u[TMAX];
 #pragma unroll
@@ -899,7 +904,7 @@ __device__ __forceinline__ void xpose_recur(const floatx4 (&D)[R / 2], const Sta
 // dot products on the matrix cores (tiles of 64 or 128 value rows).
 template <int R, int BV, int TMAX, int NT>
 __device__ __forceinline__ void chunk_verify_mfma(const float (&S)[R][16], StageChunk<BV, NT>& st,
-                                                  XBuf<R>& xb, const Params& p, const Ctx& c, int T,
+                                                  XBuf<R, BV / (8 * R)>& xb, const Params& p, const Ctx& c, int T,
                                                   long long tok0) {
   static_assert(R >= 2, "the matrix-core path takes 16 value rows per wave");
   coef_phase<BV, TMAX, NT>(st, c, T);
@@ -932,13 +937,13 @@ constexpr uint16_t kBf16NaN = 0x7FC0;
 
 template <int BV>
 __device__ __forceinline__ void poison_row(const Params& p, const Ctx& c, int T) {
-  for (int i = c.tid; i < T * BV; i += NTHREADS) {
+  for (int i = c.tid; i < T * BV; i += (int)blockDim.x) {
     const int t = i / BV, vr = i - t * BV;
     p.o[((long long)(c.bos + t) * c.H + c.head) * KD + c.tile * BV + vr] = kBf16NaN;
   }
   if (c.tile == 0) {
     const int n = T < p.Q ? T : p.Q;
-    for (int t = c.tid; t < n; t += NTHREADS)
+    for (int t = c.tid; t < n; t += (int)blockDim.x)
       p.rb[((long long)c.ri * c.H + c.head) * p.Q + t] = kBf16NaN;
   }
 }
@@ -985,9 +990,9 @@ __device__ __forceinline__ bool commit_now(const Params& p, int row) {
 // and beta records of a row longer than the bound (poison_row). (The
 // same cut in the deferred verify, 106 -> 96 VGPRs at 64-row tiles, ran 3%
 // slower: the extra resident workgroups contend in its fold and store.)
-template <int MODE, int R, int TMAX, bool SHORT = false>
+template <int MODE, int R, int TMAX, bool SHORT = false, int NW = NWAVES>
 __device__ __forceinline__ void kda_block(const Params& p, int b) {
-  constexpr int BV = R * NWAVES * 8;   // value rows per workgroup
+  constexpr int BV = R * NW * 8;   // value rows per workgroup (NW waves)
   constexpr bool kChunk = (MODE == kVerify || MODE == kDeferred);
   // tokens staged at a time: the verify modes stage one chunk of a window
   // (TMAX) and replay records in chunks of the same size; the other modes
@@ -997,7 +1002,7 @@ __device__ __forceinline__ void kda_block(const Params& p, int b) {
   __shared__ StageT st;
   // the matrix-core verify's per-wave LDS
   struct NoXBuf {};
-  using XBufT = typename std::conditional<(kChunk && R >= 2), XBuf<R>, NoXBuf>::type;
+  using XBufT = typename std::conditional<(kChunk && R >= 2), XBuf<R, NW>, NoXBuf>::type;
   __shared__ XBufT xbuf;
 
   Ctx c;
@@ -1221,15 +1226,15 @@ __device__ __forceinline__ int logical_block(int nb) {
 // compiler's choice (5 waves per SIMD); held to 6 waves it fits in 76
 // without spills and runs 2% faster (decode workload; 7 or 8 waves need
 // spills and run 11% and 38% slower).
-template <int MODE, int R, int TMAX, bool SHORT>
+template <int MODE, int R, int TMAX, bool SHORT, int NW>
 constexpr int kda_waves() {
-  return (MODE == kVerify && SHORT && TMAX == 4 && R == 2) ? 6 : 1;
+  return (MODE == kVerify && SHORT && TMAX == 4 && R == 2 && NW == 4) ? 6 : 1;
 }
 
-template <int MODE, int R, int TMAX, bool SHORT = false>
-__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(kda_waves<MODE, R, TMAX, SHORT>())))
+template <int MODE, int R, int TMAX, bool SHORT = false, int NW = NWAVES>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kda_waves<MODE, R, TMAX, SHORT, NW>())))
 void kda_kernel(Params p) {
-  kda_block<MODE, R, TMAX, SHORT>(p, logical_block(p.total_blocks));
+  kda_block<MODE, R, TMAX, SHORT, NW>(p, logical_block(p.total_blocks));
 }
 
 // The same work for several layers in one grid: logical block b belongs to
@@ -1614,19 +1619,19 @@ int tile_rows_for(int mode, long long pairs) {
   }
   if (forced > 0) return forced;
   if (mode == kCommit || mode == kRecurrent || mode == kSpec) return 32;
-  if (mode == kVerify && pairs >= 4096) return 128;
+  if ((mode == kVerify && pairs >= 4096) || (mode == kDeferred && pairs >= 512)) return 128;
   return pairs >= 512 ? 64 : 32;
 }
 
-template <int MODE, int R, int TMAX, bool SHORT = false>
+template <int MODE, int R, int TMAX, bool SHORT = false, int NW = NWAVES>
 kda_status launch_r(Params& p, hipStream_t stream) {
-  p.tiles = KD / (32 * R);
+  p.tiles = KD / (R * NW * 8);
   const long long blocks = (long long)p.num_rows * p.H * p.tiles;
   if (blocks > 0x7FFFFFFFLL) return KDA_ERR_SHAPE;
   p.total_blocks = (int)blocks;
   void* args[] = {&p};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel<MODE, R, TMAX, SHORT>),
-                                       dim3((unsigned)blocks), dim3(NTHREADS), args, 0, stream);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel<MODE, R, TMAX, SHORT, NW>),
+                                       dim3((unsigned)blocks), dim3(NW * 64), args, 0, stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -1639,7 +1644,15 @@ kda_status launch_t(Params& p, hipStream_t stream) {
   switch (tile_rows_for(MODE, (long long)p.num_rows * p.H)) {
     case 32: return launch_r<MODE, 1, TMAX, SHORT>(p, stream);
     case 64: return launch_r<MODE, 2, TMAX, SHORT>(p, stream);
-    default: return launch_r<MODE, 4, TMAX, SHORT>(p, stream);
+    default:
+      // the deferred verify of 4-token windows on 128-row tiles runs as 8
+      // waves of 16 rows (decode workload: 58.2 -> 55.7 us against 64-row
+      // tiles of 4 waves; B = 512: 324.9 -> 322.9 us); with 8-token windows
+      // it keeps 64-row tiles (128 rows in 8 waves: 1% slower on the
+      // deep-draft and ragged workloads); the verify takes 4 waves of 32
+      if constexpr (MODE == kDeferred && TMAX == 4) return launch_r<MODE, 2, TMAX, SHORT, 8>(p, stream);
+      else if constexpr (MODE == kDeferred) return launch_r<MODE, 2, TMAX, SHORT>(p, stream);
+      else return launch_r<MODE, 4, TMAX, SHORT>(p, stream);
   }
 }
 
@@ -1665,7 +1678,8 @@ kda_status launch_layers(Params& p, LayerTable& t, int num_layers, hipStream_t s
   switch (tile_rows_for(MODE, (long long)p.num_rows * p.H)) {
     case 32: return launch_layers_r<MODE, 1, TMAX>(p, t, num_layers, stream);
     case 64: return launch_layers_r<MODE, 2, TMAX>(p, t, num_layers, stream);
-    default: return launch_layers_r<MODE, 4, TMAX>(p, t, num_layers, stream);
+    // (the flush keeps 64-row tiles where the deferred verify takes 128)
+    default: return launch_layers_r<MODE, MODE == kDeferred ? 2 : 4, TMAX>(p, t, num_layers, stream);
   }
 }
 
