@@ -1253,8 +1253,8 @@ __device__ __forceinline__ void apply_layer(Params& p, const LayerRef& L) {
   p.pk = L.pk; p.pv = L.pv; p.pg = L.pg; p.pb = L.pb;
 }
 
-template <int MODE, int R, int TMAX>
-__global__ __launch_bounds__(NTHREADS) void kda_kernel_layers(Params p, LayerTable t) {
+template <int MODE, int R, int TMAX, int NW = NWAVES>
+__global__ __launch_bounds__(NW * 64) void kda_kernel_layers(Params p, LayerTable t) {
   int b = logical_block(p.total_blocks);
   const int l = b / p.layer_blocks;
   b -= l * p.layer_blocks;
@@ -1263,7 +1263,7 @@ __global__ __launch_bounds__(NTHREADS) void kda_kernel_layers(Params p, LayerTab
   // the state indices, so every layer would write the same counts): layer 0
   // writes it
   if (l != 0) p.pending_skip = 1;
-  kda_block<MODE, R, TMAX>(p, b);
+  kda_block<MODE, R, TMAX, false, NW>(p, b);
 }
 
 // Commit over a list of rows. A deferring commit replays records for the
@@ -1642,7 +1642,10 @@ kda_status launch_r(Params& p, hipStream_t stream) {
 template <int MODE, int TMAX, bool SHORT = false>
 kda_status launch_t(Params& p, hipStream_t stream) {
   switch (tile_rows_for(MODE, (long long)p.num_rows * p.H)) {
-    case 32: return launch_r<MODE, 1, TMAX, SHORT>(p, stream);
+    // (the single-layer commit as the multi-layer one: 8 waves, 54.9 ->
+    // 54.4 us; the recurrence kernels keep 4, the stock step ran 1.6%
+    // slower with 8)
+    case 32: return launch_r<MODE, 1, TMAX, SHORT, (MODE == kCommit ? 8 : NWAVES)>(p, stream);
     case 64: return launch_r<MODE, 2, TMAX, SHORT>(p, stream);
     default:
       // the deferred verify of 4-token windows on 128-row tiles runs as 8
@@ -1656,17 +1659,17 @@ kda_status launch_t(Params& p, hipStream_t stream) {
   }
 }
 
-template <int MODE, int R, int TMAX>
+template <int MODE, int R, int TMAX, int NW = NWAVES>
 kda_status launch_layers_r(Params& p, LayerTable& t, int num_layers, hipStream_t stream) {
-  p.tiles = KD / (32 * R);
+  p.tiles = KD / (R * NW * 8);
   const long long per = (long long)p.num_rows * p.H * p.tiles;
   const long long blocks = per * num_layers;
   if (blocks > 0x7FFFFFFFLL) return KDA_ERR_SHAPE;
   p.layer_blocks = (int)per;
   p.total_blocks = (int)blocks;
   void* args[] = {&p, &t};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel_layers<MODE, R, TMAX>),
-                                       dim3((unsigned)blocks), dim3(NTHREADS), args, 0, stream);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_kernel_layers<MODE, R, TMAX, NW>),
+                                       dim3((unsigned)blocks), dim3(NW * 64), args, 0, stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -1676,7 +1679,11 @@ template <int MODE>
 kda_status launch_layers(Params& p, LayerTable& t, int num_layers, hipStream_t stream) {
   constexpr int TMAX = MODE == kDeferred ? 4 : CH;   // the fold does not use the chunk path
   switch (tile_rows_for(MODE, (long long)p.num_rows * p.H)) {
-    case 32: return launch_layers_r<MODE, 1, TMAX>(p, t, num_layers, stream);
+    // the commit's smallest tiles as 8 waves of 8 rows (64 rows per
+    // workgroup, one record staging for all of them): the decode
+    // workload's 12-layer commit 540.9 -> 520.2 us against 32-row tiles of
+    // 4 waves (2 waves: 531.1, 16 waves: 520.6)
+    case 32: return launch_layers_r<MODE, 1, TMAX, (MODE == kCommit ? 8 : NWAVES)>(p, t, num_layers, stream);
     case 64: return launch_layers_r<MODE, 2, TMAX>(p, t, num_layers, stream);
     // (the flush keeps 64-row tiles where the deferred verify takes 128)
     default: return launch_layers_r<MODE, MODE == kDeferred ? 2 : 4, TMAX>(p, t, num_layers, stream);
