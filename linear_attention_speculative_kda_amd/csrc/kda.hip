@@ -8,12 +8,13 @@
 //
 // Kernel design (one kernel body serves the recurrent, verify, commit and
 // deferred calls, single- or multi-layer):
-//  * One workgroup of 256 threads (4 waves) per (request row, head, V-tile of
-//    BV = 32*R value rows). The fp32 K x BV state tile lives in VGPRs: a group
-//    of 8 adjacent lanes owns one value row; each lane holds 16 key channels
-//    of it (4 chunks of 4 consecutive channels, chunk j at j*32 + 4*(lane%8)),
-//    so one 128-bit load per chunk and the 8 lanes of a group read 128
-//    contiguous bytes. Each lane holds R rows.
+//  * One workgroup of NW waves (4; 8 for the commit and for the deferred
+//    verify of 4-token windows on 128-row tiles) per (request row, head,
+//    V-tile of BV = 8*R*NW value rows). The fp32 K x BV state tile lives in
+//    VGPRs: a group of 8 adjacent lanes owns one value row; each lane holds
+//    16 key channels of it (4 chunks of 4 consecutive channels, chunk j at
+//    j*32 + 4*(lane%8)), so one 128-bit load per chunk and the 8 lanes of a
+//    group read 128 contiguous bytes. Each lane holds R rows, whatever NW.
 //  * The per-token vectors shared by all rows (k^, q^, exp(g), beta and the
 //    tile's slice of v) are computed once per workgroup, 8 tokens at a time,
 //    by half-waves (one token each, 4 channels per lane) into LDS. The token
@@ -39,11 +40,12 @@
 //  * The state is streamed: the verify's tile loads and the commit's and
 //    deferred fold's loads and stores are non-temporal, since every
 //    checkpoint is touched once per kernel and step.
-//  * Matrix cores only for the verify of 8-token chunks, where the 16 dot
-//    products per value row bound the vector lanes (fp32 MFMA). Elsewhere the
-//    work per state element is a handful of FMAs against a state read once
-//    and written at most once: bound by HBM bandwidth, and the matrix cores
-//    ran no faster there (measured).
+//  * Matrix cores (fp32 MFMA) for the verify's dot products on tiles of 16
+//    or more rows per wave: each wave moves its rows through its own LDS
+//    into the operand layout, so the tile still loads in whole lines. The
+//    per-token replay (commit, recurrence, fold) is a handful of FMAs per
+//    state element against a state read once and written at most once:
+//    bound by HBM bandwidth, on the vector lanes.
 //  * -ffp-contract=off: every FMA is an explicit fmaf, nothing is contracted
 //    or reassociated by the compiler.
 //  * Every index read from device memory (cu_seqlens, slots, record rows,
