@@ -1281,8 +1281,8 @@ __global__ __launch_bounds__(NW * 64) void kda_kernel_layers(Params p, LayerTabl
 // counts of all rows, as the first layer's workgroups do in the full grid.
 constexpr int kListRows = 2048;
 
-template <int R>
-__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(R == 1 ? 5 : 1)))
+template <int R, int NW = NWAVES>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(R == 1 ? 5 : 1)))
 void kda_commit_list(Params p, LayerTable t, int num_layers) {
   __shared__ unsigned long long mask[kListRows / 64];
   __shared__ unsigned short list[kListRows];
@@ -1291,7 +1291,7 @@ void kda_commit_list(Params p, LayerTable t, int num_layers) {
   const int nchunks = (p.num_rows + 63) >> 6;
   const bool write_pending = p.pending != nullptr && blockIdx.x == 0;
   const int slots0 = t.l[0].num_slots;
-  for (int k = wave; k < nchunks; k += NWAVES) {
+  for (int k = wave; k < nchunks; k += NW) {
     const int row = k * 64 + lane;
     bool work = false;
     if (row < p.num_rows) {
@@ -1314,7 +1314,7 @@ void kda_commit_list(Params p, LayerTable t, int num_layers) {
   int count = 0;
   for (int k = 0; k < nchunks; ++k) {
     const unsigned long long m = mask[k];
-    if ((k & (NWAVES - 1)) == wave && ((m >> lane) & 1ull))
+    if ((k & (NW - 1)) == wave && ((m >> lane) & 1ull))
       list[count + __popcll(m & ((1ull << lane) - 1ull))] = (unsigned short)(k * 64 + lane);
     count += __popcll(m);
   }
@@ -1330,7 +1330,7 @@ void kda_commit_list(Params p, LayerTable t, int num_layers) {
     const int l = rem / per_layer;
     rem -= l * per_layer;
     apply_layer(p, t.l[l]);
-    kda_block<kCommit, R, CH>(p, (int)list[e] * per_layer + rem);
+    kda_block<kCommit, R, CH, false, NW>(p, (int)list[e] * per_layer + rem);
   }
 }
 
@@ -1707,9 +1707,9 @@ bool commit_by_list(const Params& p) {
   return forced >= 0 ? forced == 1 : p.pending != nullptr;
 }
 
-// Workgroups of kda_commit_list<R> resident at once on the current device
+// Workgroups of kda_commit_list<R, NW> resident at once on the current device
 // (compute units x workgroups per unit), queried once per device.
-template <int R>
+template <int R, int NW>
 int list_capacity() {
   constexpr int kDevices = 64;
   static int cap[kDevices] = {};
@@ -1718,7 +1718,7 @@ int list_capacity() {
   if (dev < kDevices && cap[dev] > 0) return cap[dev];
   int occ = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &occ, reinterpret_cast<const void*>(&kda_commit_list<R>), NTHREADS, 0) != hipSuccess ||
+          &occ, reinterpret_cast<const void*>(&kda_commit_list<R, NW>), NW * 64, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   const int c = occ * cus;
@@ -1726,23 +1726,25 @@ int list_capacity() {
   return c;
 }
 
-template <int R>
+template <int R, int NW = NWAVES>
 kda_status launch_list_r(Params& p, LayerTable& t, int num_layers, hipStream_t stream) {
-  p.tiles = KD / (32 * R);
+  p.tiles = KD / (R * NW * 8);
   const long long full = (long long)p.num_rows * p.H * p.tiles * num_layers;
-  long long grid = list_capacity<R>();
+  long long grid = list_capacity<R, NW>();
   if (grid < 1) return KDA_ERR_LAUNCH;
   if (grid > full) grid = full;
   p.total_blocks = (int)grid;
   void* args[] = {&p, &t, &num_layers};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_commit_list<R>),
-                                       dim3((unsigned)grid), dim3(NTHREADS), args, 0, stream);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_commit_list<R, NW>),
+                                       dim3((unsigned)grid), dim3(NW * 64), args, 0, stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status launch_list(Params& p, LayerTable& t, int num_layers, hipStream_t stream) {
   switch (tile_rows_for(kCommit, (long long)p.num_rows * p.H)) {
-    case 32: return launch_list_r<1>(p, t, num_layers, stream);
+    // 8 waves of 8 rows, as the full-grid commit (B = 512 deferred
+    // workload: deferred flow 398.0 -> 392.4 us per layer-step)
+    case 32: return launch_list_r<1, 8>(p, t, num_layers, stream);
     case 64: return launch_list_r<2>(p, t, num_layers, stream);
     default: return launch_list_r<4>(p, t, num_layers, stream);
   }
